@@ -1,0 +1,137 @@
+"""CPU oracle for fused softmax attention: TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The GPU library never imports, links or calls it, and
+this package imports nothing from the GPU library: the two share no code.
+
+Contents
+  attn_oracle.c  plain fp64 three-pass forward and analytic backward (C, OpenMP)
+  monoid.py      the online-softmax state (m, l, acc) and its combine rule
+  brute.py       50-digit mpmath evaluation of the definition (no max shift)
+
+The C library is compiled with the host gcc into ``liboracle.so`` next to this
+file.  ``build()`` compiles it unconditionally; ``lib()`` compiles it only if no
+build exists yet (or the source is newer than the build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile attn_oracle.c with gcc -O2 -fopenmp into liboracle.so."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(
+        ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"],
+        check=True,
+    )
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    L = ctypes.CDLL(_LIB)
+    i64, f64, vp, ci = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+    L.oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f64, ci]
+    L.oracle_fwd_rows.argtypes = [vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64, i64, i64, f64, ci]
+    L.oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f64, ci]
+    L.oracle_bwd_rowdot.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f64, ci]
+    for f in (L.oracle_fwd, L.oracle_fwd_rows, L.oracle_bwd, L.oracle_bwd_rowdot, L.oracle_num_threads):
+        f.restype = ci
+    _lib = L
+    return L
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dims(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch between q, k, v")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def fwd(q, k, v, scale: float, causal: bool):
+    """Three-pass softmax attention.  Returns (O [B,Hq,Nq,d], LSE [B,Hq,Nq]) in fp64."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    o = np.empty((B, Hq, Nq, d), np.float64)
+    lse = np.empty((B, Hq, Nq), np.float64)
+    rc = lib().oracle_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, Nq, Nk, d, float(scale), int(causal))
+    if rc:
+        raise ValueError(f"oracle_fwd rejected its arguments ({rc})")
+    return o, lse
+
+
+def fwd_rows(q, k, v, rows, scale: float, causal: bool):
+    """Forward on selected rows.  rows: int array [n, 3] of (b, h, i).  Returns (O [n,d], LSE [n])."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    n = rows.shape[0]
+    o = np.empty((n, d), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = lib().oracle_fwd_rows(_p(q), _p(k), _p(v), _p(rows), n, _p(o), _p(lse), B, Hq, Hkv, Nq, Nk, d,
+                               float(scale), int(causal))
+    if rc:
+        raise ValueError(f"oracle_fwd_rows rejected its arguments ({rc})")
+    return o, lse
+
+
+def bwd(q, k, v, dout, scale: float, causal: bool):
+    """Analytic gradient of sum(dout * O).  Returns (dQ, dK, dV) in fp64."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    dq = np.empty((B, Hq, Nq, d), np.float64)
+    dk = np.empty((B, Hkv, Nk, d), np.float64)
+    dv = np.empty((B, Hkv, Nk, d), np.float64)
+    rc = lib().oracle_bwd(_p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv), B, Hq, Hkv, Nq, Nk, d,
+                          float(scale), int(causal))
+    if rc:
+        raise ValueError(f"oracle_bwd rejected its arguments ({rc})")
+    return dq, dk, dv
+
+
+def rowdot(q, k, v, dout, scale: float, causal: bool):
+    """D_i = sum_j P_ij (dO_i . V_j), from the definition.  Returns [B,Hq,Nq] fp64."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    out = np.empty((B, Hq, Nq), np.float64)
+    rc = lib().oracle_bwd_rowdot(_p(q), _p(k), _p(v), _p(dout), _p(out), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                 int(causal))
+    if rc:
+        raise ValueError(f"oracle_bwd_rowdot rejected its arguments ({rc})")
+    return out
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel regions use."""
+    return int(lib().oracle_num_threads())

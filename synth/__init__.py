@@ -1,0 +1,80 @@
+"""Seeded synthetic inputs shared by the GPU library's tests/benchmark and the oracle.
+
+This module holds no attention arithmetic: it draws i.i.d. standard normal
+tensors from a seeded numpy generator, rounds them to bfloat16 when asked, and
+picks sampled row indices.  Both sides of every comparison receive the same
+bits from here.
+
+Recipe (also stated in the design doc):
+  * ``numpy.random.default_rng(seed).standard_normal(shape, float32)``, drawn
+    in the order the caller lists the tensors (Q, K, V, dO by convention);
+  * bf16 inputs are those fp32 draws rounded to nearest-even bfloat16; the
+    fp32 arrays returned then hold exactly the bf16 values.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns (uint16), round to nearest even.  Inputs must be finite."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> the exact fp32 values."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal(seed: int, shapes, bf16: bool, scale: float = 1.0):
+    """Draw tensors of the given shapes, in order, from one generator.
+
+    Returns a list of fp32 arrays.  With ``bf16`` the values are rounded to
+    bfloat16 (so each fp32 array holds exact bf16 values).  ``scale``
+    multiplies the draws before rounding (used for peaked inputs).
+    """
+    rng = np.random.default_rng(seed)
+    out = []
+    for shp in shapes:
+        x = rng.standard_normal(shp, dtype=np.float32)
+        if scale != 1.0:
+            x = (x * np.float32(scale)).astype(np.float32)
+        if bf16:
+            x = bf16_bits_to_f32(round_bf16_bits(x)).reshape(shp)
+        out.append(x)
+    return out
+
+
+def attn_inputs(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, bf16: bool, with_dout: bool = False,
+                scale: float = 1.0):
+    """Q [B,Hq,Nq,d], K, V [B,Hkv,Nk,d] (and dO [B,Hq,Nq,d]) drawn in that order."""
+    shapes = [(B, Hq, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d)]
+    if with_dout:
+        shapes.append((B, Hq, Nq, d))
+    return normal(seed, shapes, bf16, scale)
+
+
+def sample_rows(seed: int, n: int, B: int, Hq: int, Nq: int, forced_i=()) -> np.ndarray:
+    """n distinct (b, h, i) triples from a generator separate from the data's.
+
+    The positions in ``forced_i`` come first (each at a random b, h); the rest
+    are uniform.  Returns int64 [n, 3].
+    """
+    rng = np.random.default_rng(seed)
+    seen = set()
+    rows = []
+    for i in forced_i:
+        if 0 <= i < Nq:
+            t = (int(rng.integers(B)), int(rng.integers(Hq)), int(i))
+            if t not in seen:
+                seen.add(t)
+                rows.append(t)
+    while len(rows) < n:
+        t = (int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Nq)))
+        if t not in seen:
+            seen.add(t)
+            rows.append(t)
+    return np.array(rows[:n], np.int64)
