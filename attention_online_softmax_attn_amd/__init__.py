@@ -1,0 +1,175 @@
+"""Python binding of the MI355X fused softmax-attention library (libattn_mi355x.so).
+
+Argument marshalling only: tensors are checked and allocated with PyTorch (ROCm)
+for device memory, and every step of the computation runs in the library's HIP
+kernels on the current PyTorch stream.  There is no CPU path: if the library is
+not built, or a tensor is not on the GPU, these functions raise.
+
+    attn_fwd(q, k, v, causal, scale)                  -> (o, lse)
+    attn_decode_splitkv(q, k, v, scale, num_splits=0) -> (o, lse)
+    attn_bwd(q, k, v, o, dout, lse, causal, scale)    -> (dq, dk, dv)
+
+Layouts are [B, H, N, d] contiguous (q/o/dout/dq with Hq heads, k/v/dk/dv with
+Hkv heads); lse is [B, Hq, Nq] fp32; gradients are fp32.  See include/attn.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_F32, ATTN_BF16 = 0, 1
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m attention_online_softmax_attn_amd.build`"
+        )
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci, vp]
+    L.attn_fwd.restype = ci
+    L.attn_decode_num_splits.argtypes = [i64, i64, i64, i64, i64]
+    L.attn_decode_num_splits.restype = ci
+    L.attn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci, vp, sz, ci, vp]
+    L.attn_decode_splitkv.restype = ci
+    L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, vp, sz, ci, vp]
+    L.attn_bwd.restype = ci
+    L.attn_strerror.argtypes = [ci]
+    L.attn_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().attn_strerror(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU; there is no CPU path")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+
+
+def _dims(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    return B, Hq, k.shape[1], Nq, k.shape[2], d
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale=None, out=None, lse=None, want_lse: bool = True):
+    """Fused forward.  Returns (o, lse); lse is None when want_lse is False."""
+    _check_dev(q, k, v, out, lse)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if want_lse else None, B, Hq, Hkv, Nq, Nk,
+                        d, _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+    return o, (lse if want_lse else None)
+
+
+def decode_num_splits(B: int, Hq: int, Hkv: int, Nk: int, d: int) -> int:
+    return int(lib().attn_decode_num_splits(B, Hq, Hkv, Nk, d))
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits))
+
+
+def attn_decode_splitkv(q, k, v, scale=None, num_splits: int = 0, workspace=None, out=None, lse=None,
+                        want_lse: bool = True):
+    """Split-KV decode (q has Nq = 1).  Returns (o, lse)."""
+    _check_dev(q, k, v, out, lse, workspace)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if want_lse else None, B, Hq, Hkv,
+                                   Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _ptr(workspace), ws_bytes,
+                                   _dtype_code(q), _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_splitkv")
+    return o, (lse if want_lse else None)
+
+
+def bwd_workspace_bytes(B: int, Hq: int, Nq: int, d: int) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Nq, d))
+
+
+def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale=None, workspace=None, dq=None, dk=None, dv=None):
+    """Backward from the saved LSE.  Returns fp32 (dq, dk, dv)."""
+    _check_dev(q, k, v, o, dout, lse, workspace, dq, dk, dv)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32) if dq is None else dq
+    dk = torch.empty(k.shape, **f32) if dk is None else dk
+    dv = torch.empty(v.shape, **f32) if dv is None else dv
+    need = bwd_workspace_bytes(B, Hq, Nq, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B,
+                        Hq, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _ptr(workspace), ws_bytes,
+                        _dtype_code(q), _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

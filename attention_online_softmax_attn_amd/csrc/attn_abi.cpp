@@ -1,0 +1,193 @@
+// C ABI of the attention library: argument validation (host only, before any
+// HIP call), the split-KV plan, workspace layout and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kNumCUs = 256;  // MI355X compute units; the split plan targets whole waves of workgroups
+
+bool dims_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk) {
+  return B >= 0 && Hq >= 1 && Hkv >= 1 && Nq >= 0 && Nk >= 0 && Hq % Hkv == 0;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+
+// Common checks; returns ATTN_OK when the call may proceed.
+attn_status check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                         attn_dtype dtype) {
+  if (!dims_ok(B, Hq, Hkv, Nq, Nk)) return ATTN_ERR_INVALID;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (Nq > ATTN_MAX_SEQ || Nk > ATTN_MAX_SEQ) return ATTN_ERR_UNSUPPORTED;
+  // grid sizes must fit in 32-bit workgroup counts
+  if (B * Hq > (int64_t)1 << 20) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+struct SplitPlan {
+  int splits;
+  int chunk;
+};
+
+// Choose the number of key chunks per (b, kv head): the smallest count whose
+// total workgroup count fills the GPU's workgroup slots in the most nearly
+// whole waves, keeping at least 4 key tiles per chunk.
+SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int requested) {
+  const int tile = attn::kDecodeTile;
+  const int64_t tiles = Nk > 0 ? (Nk + tile - 1) / tile : 1;
+  int s;
+  if (requested > 0) {
+    s = requested;
+  } else {
+    const int64_t units = B * Hkv;
+    const int64_t s_max = std::max<int64_t>(1, tiles / 4);
+    double best = -1.0;
+    s = 1;
+    for (int64_t c = 1; c <= std::min<int64_t>(s_max, 64); c++) {
+      const int64_t wgs = units * c;
+      const double waves = (double)wgs / kNumCUs;
+      const double eff = waves / std::ceil(waves);
+      if (eff > best + 1e-9) {
+        best = eff;
+        s = (int)c;
+      }
+      if (wgs >= 4 * kNumCUs) break;
+    }
+  }
+  if (s > tiles) s = (int)tiles;
+  int64_t chunk = ((tiles + s - 1) / s) * tile;
+  int eff = Nk > 0 ? (int)((Nk + chunk - 1) / chunk) : 1;
+  return {eff, (int)chunk};
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_strerror(attn_status status) {
+  switch (status) {
+    case ATTN_OK:
+      return "ok";
+    case ATTN_ERR_INVALID:
+      return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case ATTN_ERR_HIP:
+      return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, attn_dtype dtype,
+                     void* stream) {
+  attn_status st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  if (!q || !o || (Nk > 0 && (!k || !v))) return ATTN_ERR_INVALID;
+  attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, dtype == ATTN_BF16};
+  return attn::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_decode_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d) {
+  if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128)) return -1;
+  return plan_splits(B, Hkv, Nk, 0).splits;
+}
+
+size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
+  if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128) || num_splits < 0) return 0;
+  SplitPlan sp = plan_splits(B, Hkv, Nk, num_splits);
+  if (sp.splits <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * sp.splits;
+  return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                                int num_splits, void* workspace, size_t workspace_bytes, attn_dtype dtype,
+                                void* stream) {
+  (void)causal;  // one bottom-right-aligned query sees every key
+  attn_status st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0) return ATTN_ERR_INVALID;
+  if (Nq != 1 && !(Nq == 0 || B == 0)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 32) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  if (!q || !o || (Nk > 0 && (!k || !v))) return ATTN_ERR_INVALID;
+  SplitPlan sp = plan_splits(B, Hkv, Nk, num_splits);
+  attn::DecodeProblem p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nk = Nk;
+  p.d = d;
+  p.scale = scale;
+  p.num_splits = sp.splits;
+  p.chunk = sp.chunk;
+  if (sp.splits > 1) {
+    const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits);
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t rows = (size_t)B * Hq * sp.splits;
+    p.part_acc = (float*)workspace;
+    p.part_ml = (float*)((char*)workspace + align256(rows * d * sizeof(float)));
+  }
+  return attn::launch_decode(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d) {
+  if (B < 0 || Hq < 1 || Nq < 0 || (d != 64 && d != 128)) return 0;
+  return align256((size_t)B * Hq * Nq * sizeof(float));
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     float* dq, float* dk, float* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                     int64_t d, float scale, int causal, void* workspace, size_t workspace_bytes, attn_dtype dtype,
+                     void* stream) {
+  attn_status st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+  if (Nq > 0 && (!q || !o || !dout || !lse || !dq)) return ATTN_ERR_INVALID;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID;
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq, d);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  attn::BwdProblem p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = (float*)workspace;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal ? 1 : 0;
+  return attn::launch_bwd(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,284 @@
+// Split-KV decode kernels for gfx950.
+//
+// One query token per stream.  A kv head's Nk keys are cut into num_splits
+// chunks; workgroup (b, kv head, split) streams its chunk of K and V from HBM
+// exactly once and serves all g = Hq / Hkv query heads that share the kv head
+// (grouped-query packing: the g queries are the columns of one MFMA tile, so
+// the bytes read do not grow with g).  The four waves of a workgroup take
+// 32-key tiles in turn, each through its own pair of LDS buffers filled by
+// direct-to-LDS buffer loads, and each keeps its own online-softmax state
+// (m, l, acc).  At the end the four states are folded with the monoid rule
+// through LDS; the result is either the final output (one split) or a partial
+// state written to the workspace, and a merge kernel folds the splits:
+//
+//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  acc = sum_s acc_s 2^(m_s - M),
+//   O = acc / L,    LSE = (M + log2 L) ln 2,
+//
+// with a split whose m_s = -inf contributing nothing.  The fold is the
+// online-softmax monoid of "Não escreva kernels, derive-os" (section
+// "Aprofundamento", first paragraph); the decode setting with 1 to 48
+// concurrent streams is the one "Tang Project Derives GPU Kernels via IR ..."
+// reports in its "Details" section.  Regrouping a monoid fold does not change
+// its value, so any split count gives the same result up to rounding.
+#include "device_common.hpp"
+#include "kernels.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kTau = 8.0f;
+constexpr int kWaves = 4;
+
+struct DecArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  float* part_acc;
+  float* part_ml;
+  int B, Hq, Hkv, Nk, g;
+  int S, chunk, n_wgs;
+  float c;
+};
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs a) {
+  constexpr int BN = kDecodeTile;
+  constexpr int TILE_BYTES = BN * D * 2;
+  constexpr int STAGE = 2 * TILE_BYTES;  // K then V
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = BN * CPR / 64;   // per lane per tile, one wave loads its own tile
+  static_assert(BN == 32, "one 32-key MFMA block per tile");
+  // per wave: two stages; the same memory is reused for the final fold
+  __shared__ __attribute__((aligned(1024))) char smem[kWaves * 2 * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h32 = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int work = xcd_remap(blockIdx.x, a.n_wgs);
+  const int split = work % a.S;
+  const int pair = work / a.S;
+  const int b = pair / a.Hkv;
+  const int kvh = pair % a.Hkv;
+
+  const int k0 = split * a.chunk;
+  const int k1 = min(a.Nk, k0 + a.chunk);
+  const int n_tiles = k1 > k0 ? (k1 - k0 + BN - 1) / BN : 0;
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+
+  const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)a.Nk * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)a.Nk * D * 2);
+  const size_t q_grp = ((size_t)b * a.Hq + (size_t)kvh * a.g) * D;  // the g query rows of this kv head
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_grp, (uint32_t)a.g * D * 2);
+
+  char* wbase = smem + wave * 2 * STAGE;
+
+  auto issue = [&](int i, char* kt, char* vt) {
+    const int j0 = k0 + (wave + kWaves * i) * BN;
+#pragma unroll
+    for (int n = 0; n < LOADS; n++) {
+      const int p = n * 64 + lane;
+      const int r = p / CPR;
+      const int cc = (p % CPR) ^ swz<D>(r);
+      const uint32_t src = (uint32_t)(((j0 + r) * D + cc * 8) * 2);
+      buf_load_lds16(rk, src, (lds_void*)(kt + n * 1024));
+      buf_load_lds16(rv, src, (lds_void*)(vt + n * 1024));
+    }
+  };
+
+  if (my_tiles > 0) issue(0, wbase, wbase + TILE_BYTES);
+
+  // query fragments: column l32 is query head kvh*g + l32 (zero beyond g)
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; s++)
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)((l32 * D + 16 * s + 8 * h32) * 2)));
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
+  float m_run = kNegInf, l_run = 0.0f;
+  const int swl = swz<D>(l32);
+
+  auto compute = [&](int i, const char* kt, const char* vt) {
+    const int j0 = k0 + (wave + kWaves * i) * BN;
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; s++) {
+      const bf16x8 kf = *(const bf16x8*)(kt + l32 * (D * 2) + (((2 * s + h32) ^ swl) << 4));
+      st = mfma32(kf, qf[s], st);
+    }
+    if (j0 + BN > k1) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int j = j0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        if (j >= k1) st[r] = kNegInf;
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[r]);
+    mx = halves_max(mx) * a.c;
+    const bool grow = mx > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // lanes that do not grow keep their state (alpha = 1; their m_run may
+      // still be -inf); a growing lane with m_run = -inf gets alpha = 0
+      const float alpha = grow ? fast_exp2(m_run - mx) : 1.0f;
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[cb][r] *= alpha;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      st[r] = fast_exp2(__builtin_fmaf(st[r], a.c, -m_use));
+      l_run += st[r];
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; e++) pb[e] = to_bf16(st[8 * hf + e]);
+      const int vr = 16 * hf + 4 * h32 + ((lane & 15) >> 2);
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++) {
+        const int vc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const s16x4 lo = ds_read_tr16(vt + tile_off<D>(vr, vc));
+        const s16x4 hi = ds_read_tr16(vt + tile_off<D>(vr + 8, vc));
+        acc[cb] = mfma32(join_bf16(lo, hi), pb, acc[cb]);
+      }
+    }
+  };
+
+  // one step: prefetch this wave's next tile into the other stage, compute the
+  // current one (restrict: the prefetch never writes what the step reads)
+  auto step = [&](int i, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
+                  char* __restrict__ vn) {
+    wait_vmem();
+    if (i + 1 < my_tiles) issue(i + 1, kn, vn);
+    compute(i, kc, vc);
+  };
+  char* const s0 = wbase;
+  char* const s1 = wbase + STAGE;
+  for (int i = 0; i < my_tiles; i += 2) {
+    step(i, s0, s0 + TILE_BYTES, s1, s1 + TILE_BYTES);
+    if (i + 1 >= my_tiles) break;
+    step(i + 1, s1, s1 + TILE_BYTES, s0, s0 + TILE_BYTES);
+  }
+
+  // ---- fold the four wave states: the monoid rule, through LDS
+  const float l_tot = halves_sum(l_run);
+  __syncthreads();  // every wave is done with its tile buffers
+  float* f_acc = (float*)smem;                        // [kWaves][g][D]
+  float* f_m = f_acc + kWaves * 32 * D;               // [kWaves][32]
+  float* f_l = f_m + kWaves * 32;                     // [kWaves][32]
+  if (l32 < a.g) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        f_acc[(wave * 32 + l32) * D + cb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3)] = acc[cb][r];
+    if (h32 == 0) {
+      f_m[wave * 32 + l32] = m_run;
+      f_l[wave * 32 + l32] = l_tot;
+    }
+  }
+  __syncthreads();
+  const int total = a.g * D;
+  for (int e = threadIdx.x; e < total; e += kWaves * 64) {
+    const int qh = e / D, col = e % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, f_m[w * 32 + qh]);
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+      const float mw = f_m[w * 32 + qh];
+      const float f = (mw == kNegInf) ? 0.0f : fast_exp2(mw - M);
+      L += f * f_l[w * 32 + qh];
+      A += f * f_acc[(w * 32 + qh) * D + col];
+    }
+    const int hq = kvh * a.g + qh;
+    const size_t row = (size_t)b * a.Hq + hq;
+    if (a.S == 1) {
+      a.o[row * D + col] = to_bf16(L > 0.0f ? A / L : 0.0f);
+      if (col == 0 && a.lse != nullptr) a.lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    } else {
+      a.part_acc[(row * a.S + split) * D + col] = A;
+      if (col == 0) {
+        a.part_ml[(row * a.S + split) * 2 + 0] = M;
+        a.part_ml[(row * a.S + split) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Fold num_splits partial states per (b, query head).  One wave per row.
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.B * a.Hq) return;
+  const float* ml = a.part_ml + (size_t)row * a.S * 2;
+  float M = kNegInf;
+  for (int s = 0; s < a.S; s++) M = fmaxf(M, ml[2 * s]);
+  float L = 0.0f;
+  float A[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; e++) A[e] = 0.0f;
+  for (int s = 0; s < a.S; s++) {
+    const float ms = ml[2 * s];
+    const float f = (ms == kNegInf) ? 0.0f : fast_exp2(ms - M);
+    L += f * ml[2 * s + 1];
+    const float* pa = a.part_acc + ((size_t)row * a.S + s) * D;
+#pragma unroll
+    for (int e = 0; e < D / 64; e++) A[e] += f * pa[e * 64 + lane];
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+  for (int e = 0; e < D / 64; e++) a.o[(size_t)row * D + e * 64 + lane] = to_bf16(A[e] * inv);
+  if (lane == 0 && a.lse != nullptr) a.lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+}
+
+template <int D>
+hipError_t launch(const DecodeProblem& p, hipStream_t s) {
+  DecArgs a;
+  a.q = (const __bf16*)p.q;
+  a.k = (const __bf16*)p.k;
+  a.v = (const __bf16*)p.v;
+  a.o = (__bf16*)p.o;
+  a.lse = p.lse;
+  a.part_acc = p.part_acc;
+  a.part_ml = p.part_ml;
+  a.B = (int)p.B;
+  a.Hq = (int)p.Hq;
+  a.Hkv = (int)p.Hkv;
+  a.Nk = (int)p.Nk;
+  a.g = a.Hq / a.Hkv;
+  a.S = p.num_splits;
+  a.chunk = p.chunk;
+  a.n_wgs = a.B * a.Hkv * a.S;
+  a.c = p.scale * kLog2e;
+  hipLaunchKernelGGL((decode_partial_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.S == 1) return e;
+  const int rows = a.B * a.Hq;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeProblem& p, hipStream_t s) {
+  return p.d == 128 ? launch<128>(p, s) : launch<64>(p, s);
+}
+
+}  // namespace attn

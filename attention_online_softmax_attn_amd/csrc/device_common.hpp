@@ -1,0 +1,128 @@
+// Device primitives for gfx950 (MI355X): MFMA fragments, LDS tile layout,
+// buffer loads (global and direct-to-LDS), wave64 cross-half reductions.
+//
+// Lane layouts used throughout (wave64, lane = 0..63, half h = lane / 32):
+//   v_mfma_f32_32x32x16_bf16  A[m][k]: lane holds row m = lane%32, k = 8h..8h+7
+//                             B[k][n]: lane holds col n = lane%32, k = 8h..8h+7
+//                             C[m][n]: lane holds col n = lane%32, 16 rows
+//                                      m = 8(r/4) + 4h + r%4, r = 0..15
+//   v_mfma_f32_32x32x2_f32    A: row lane%32, k = h;  B: col lane%32, k = h;  C as above
+//   ds_read_b64_tr_b16        within each 16-lane group, lane t receives
+//                             element t%4 of the 8-byte words addressed by the
+//                             group's lanes 4e + t/4, e = 0..3.  With provider
+//                             lane t pointing at row r0 + t/4, column c0 + 4(t%4)
+//                             of a row-major bf16 tile, lane t receives rows
+//                             r0..r0+3 of column c0 + t: a transposed read.
+//   v_permlane32_swap         exchanges the upper half of its first operand
+//                             with the lower half of its second, so with both
+//                             operands equal lane l receives lane l^32's value
+//                             in the second result (l < 32) or the first (l >= 32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Buffer resource over [base, base + bytes); loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// 16 bytes from global byte offset `off` into LDS at lds_base + 16 * lane.
+// lds_base must be wave-uniform.
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, off, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including direct-to-LDS
+// loads) have completed; expcnt and lgkmcnt are left unconstrained.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_byte_ptr) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) char*)(lds_byte_ptr));
+}
+
+__device__ __forceinline__ bf16x8 join_bf16(s16x4 lo, s16x4 hi) {
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+  s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// x from lane l ^ 32.  After the swap the first result holds the partner's
+// value in the upper half and the second holds it in the lower half; the
+// select keeps both results live (folding them into one is wrong).
+__device__ __forceinline__ float partner32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const bool lower = (threadIdx.x & 32) == 0;
+  return __builtin_bit_cast(float, lower ? r[1] : r[0]);
+}
+// max / sum of x over lanes l and l ^ 32
+__device__ __forceinline__ float halves_max(float x) { return fmaxf(x, partner32(x)); }
+__device__ __forceinline__ float halves_sum(float x) { return x + partner32(x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16, round to nearest even (inputs here are finite or +-0).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+// 16-byte chunk swizzle of a row-major bf16 tile with rows of D elements.
+// Logical chunk c of row r is stored at chunk c ^ swz(r).  For D = 128 the
+// XOR spreads 16 consecutive rows over all 16 chunk positions (b128 reads of
+// one column chunk) and sends rows r..r+3 of an aligned 4-chunk group to 4
+// different groups (transposed b64 reads); D = 64 does the same over 8 chunks
+// and row pairs.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+}
+
+// Byte offset of element (r, c) in a swizzled [rows][D] bf16 tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * (D * 2) + ((((c >> 3) ^ swz<D>(r))) << 4) + ((c & 7) << 1);
+}
+
+// Map a launch index to a logical work index so that the workgroups the
+// dispatcher sends to one XCD (launch index mod 8) get a contiguous range of
+// logical indices.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+  constexpr int kXcd = 8;
+  int q = n / kXcd, rem = n % kXcd;
+  int x = pid % kXcd, t = pid / kXcd;
+  int start = x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q;
+  return start + t;
+}
+
+}  // namespace attn

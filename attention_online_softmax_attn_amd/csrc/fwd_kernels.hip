@@ -1,0 +1,416 @@
+// Forward prefill kernels for gfx950.
+//
+// One workgroup owns BM = 32 * NW consecutive query rows of one query head;
+// each wave owns 32 of them.  Key/value tiles of BN rows stream HBM -> LDS by
+// direct-to-LDS buffer loads into two alternating buffers, so the loads of
+// tile t+1 overlap the MFMA work of tile t.  Per tile and wave:
+//
+//   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (keys are the M dimension, so a
+//                lane holds 16 keys of one query and the softmax statistics of
+//                that query stay lane-local; the other 16 keys of the same
+//                32-key block sit in lane ^ 32)
+//   online softmax: m' = max(m, rowmax * c), p = 2^(s c - m'), l' = l 2^(m - m') + sum p
+//                (c = scale * log2 e; the max needs one permlane32 swap, the
+//                sum stays per lane until the epilogue)
+//   O^T += V^T P^T  on the same MFMA; P^T goes from the accumulator layout to
+//                the B operand without leaving registers (the key order inside
+//                the contraction is permuted identically on both operands)
+//                and V^T is read with the LDS transpose read.
+//
+// The running state (m, l, acc) is the monoid of the online softmax ("Não
+// escreva kernels, derive-os", section "Aprofundamento", first paragraph);
+// the fold over key tiles is its left fold.  Causal key tiles above a
+// workgroup's diagonal are never loaded; a wave skips the MFMA work of tiles
+// above its own diagonal; only tiles crossing a diagonal (or the end of the
+// keys) are masked elementwise.  The rescale of acc is skipped while the row
+// maximum has grown by less than kTau (log2 units): the final acc / l and
+// LSE = (m + log2 l) ln 2 are exact for any m used consistently.
+#include "device_common.hpp"
+#include "kernels.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kTau = 8.0f;
+
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, g;
+  int n_qtiles, n_wgs;
+  float c;  // scale * log2(e)
+};
+
+template <int D, int NW, int BN, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int BM = NW * 32;
+  constexpr int TILE_BYTES = BN * D * 2;       // one K or V tile
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  constexpr int LOADS = BN * CPR / (64 * NW);  // direct-to-LDS loads per thread per tile
+  static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly over the workgroup");
+  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
+
+  // buffers: [K0 | V0 | K1 | V1]
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h32 = lane >> 5;
+  const int l32 = lane & 31;
+
+  // ---- work decomposition: (b, kv head, q tile desc., head in group), XCD-grouped
+  const int work = xcd_remap(blockIdx.x, a.n_wgs);
+  const int per_pair = a.g * a.n_qtiles;
+  const int pair = work / per_pair;
+  const int rem = work % per_pair;
+  const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
+  const int hq = (pair % a.Hkv) * a.g + rem % a.g;
+  const int b = pair / a.Hkv;
+  const int kvh = pair % a.Hkv;
+
+  const int i0 = qt * BM;
+  const int qw0 = i0 + wave * 32;
+  const int off = a.Nk - a.Nq;  // causal: key j visible to query i iff j <= i + off
+
+  const size_t q_head = ((size_t)b * a.Hq + hq) * (size_t)a.Nq * D;
+  const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_head, (uint32_t)a.Nq * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)a.Nk * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)a.Nk * D * 2);
+
+  int kend = a.Nk;
+  if (CAUSAL) {
+    int last_row = min(i0 + BM, a.Nq) - 1;
+    kend = min(a.Nk, last_row + off + 1);
+  }
+  const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  // ---- issue the direct-to-LDS loads of tile t into the K/V buffers kt, vt
+  auto issue = [&](int t, char* kt, char* vt) {
+    const int j0 = t * BN;
+#pragma unroll
+    for (int n = 0; n < LOADS; n++) {
+      const int slab = n * NW + wave;  // 64 consecutive 16-byte LDS chunks
+      const int p = slab * 64 + lane;
+      const int r = p / CPR;
+      const int c = (p % CPR) ^ swz<D>(r);
+      const uint32_t src = (uint32_t)(((j0 + r) * D + c * 8) * 2);
+      buf_load_lds16(rk, src, (lds_void*)(kt + slab * 1024));
+      buf_load_lds16(rv, src, (lds_void*)(vt + slab * 1024));
+    }
+  };
+
+  if (n_tiles > 0) issue(0, smem, smem + TILE_BYTES);
+
+  // ---- Q fragments (B operand of S^T = K Q^T): row qw0 + l32, dims 16s + 8h .. +8
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; s++) {
+    const uint32_t src = (uint32_t)(((qw0 + l32) * D + 16 * s + 8 * h32) * 2);
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, src));
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
+  float m_run = kNegInf;  // log2-domain running max used for the exponentials
+  float l_run = 0.0f;     // this lane's share of the running sum
+  const int qi = qw0 + l32;
+  const int swl = swz<D>(l32);
+
+  auto compute = [&](int t, const char* kt, const char* vt) {
+    const int j0 = t * BN;
+    // wave-level classification of the tile
+    bool need_mask = (j0 + BN > a.Nk);
+    if (CAUSAL) {
+      if (j0 > qw0 + 31 + off) return;               // nothing visible to this wave
+      if (j0 + BN - 1 > qw0 + off) need_mask = true;  // crosses this wave's diagonal
+    }
+    // S^T = K Q^T
+    f32x16 st[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; kb++) st[kb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; s++) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; kb++) {
+        const int r = kb * 32 + l32;
+        const bf16x8 kf = *(const bf16x8*)(kt + r * (D * 2) + (((2 * s + h32) ^ swl) << 4));
+        st[kb] = mfma32(kf, qf[s], st[kb]);
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          bool ok = j < a.Nk;
+          if (CAUSAL) ok = ok && (j <= qi + off);
+          if (!ok) st[kb][r] = kNegInf;
+        }
+    }
+    // online softmax update
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[kb][r]);
+    mx = halves_max(mx) * a.c;
+    const bool grow = mx > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // lanes that do not grow keep their state (alpha = 1; their m_run may
+      // still be -inf); a growing lane with m_run = -inf gets alpha = 0
+      const float alpha = grow ? fast_exp2(m_run - mx) : 1.0f;
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[cb][r] *= alpha;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float p = fast_exp2(__builtin_fmaf(st[kb][r], a.c, -m_use));
+        st[kb][r] = p;
+        psum += p;
+      }
+    l_run += psum;
+    // O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; e++) pb[e] = to_bf16(st[kb][8 * hf + e]);
+        const int kk = kb * 32 + 16 * hf;
+        const int vr = kk + 4 * h32 + ((lane & 15) >> 2);
+#pragma unroll
+        for (int cb = 0; cb < D / 32; cb++) {
+          const int vc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+          const s16x4 lo = ds_read_tr16(vt + tile_off<D>(vr, vc));
+          const s16x4 hi = ds_read_tr16(vt + tile_off<D>(vr + 8, vc));
+          acc[cb] = mfma32(join_bf16(lo, hi), pb, acc[cb]);
+        }
+      }
+  };
+
+  // ---- one pipeline step: prefetch tile t+1 into the other buffers, compute
+  // tile t.  The restrict-qualified buffer pointers let the compiler see that
+  // the prefetch does not write what the tile reads, so it does not wait for
+  // the prefetch before the LDS reads.
+  auto step = [&](int t, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
+                  char* __restrict__ vn) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < n_tiles) issue(t + 1, kn, vn);
+    compute(t, kc, vc);
+  };
+  char* const b0 = smem;
+  char* const b1 = smem + 2 * TILE_BYTES;
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, b0, b0 + TILE_BYTES, b1, b1 + TILE_BYTES);
+    if (t + 1 >= n_tiles) break;
+    step(t + 1, b1, b1 + TILE_BYTES, b0, b0 + TILE_BYTES);
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qi < a.Nq) {
+    __bf16* orow = a.o + q_head + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; e++) w[e] = to_bf16(acc[cb][4 * g4 + e] * inv);
+        *(bf16x4*)(orow + cb * 32 + 8 * g4 + 4 * h32) = w;
+      }
+    if (a.lse != nullptr && h32 == 0) {
+      a.lse[((size_t)b * a.Hq + hq) * a.Nq + qi] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 forward.  Same decomposition with one wave per workgroup (32 query
+// rows) and 32-key tiles staged through LDS; contractions on
+// v_mfma_f32_32x32x2_f32, so scores, P and the accumulator stay fp32.
+struct FwdArgsF32 {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, g;
+  int n_qtiles, n_wgs;
+  float c;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgsF32 a) {
+  constexpr int BN = 32;
+  constexpr int LD = D + 1;  // padded row pitch (floats)
+  __shared__ float kt[BN * LD];
+  __shared__ float vt[BN * LD];
+  const int lane = threadIdx.x;
+  const int h32 = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int work = xcd_remap(blockIdx.x, a.n_wgs);
+  const int per_pair = a.g * a.n_qtiles;
+  const int pair = work / per_pair;
+  const int rem = work % per_pair;
+  const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
+  const int hq = (pair % a.Hkv) * a.g + rem % a.g;
+  const int b = pair / a.Hkv;
+  const int kvh = pair % a.Hkv;
+  const int qw0 = qt * 32;
+  const int off = a.Nk - a.Nq;
+  const int qi = qw0 + l32;
+
+  const float* qh = a.q + ((size_t)b * a.Hq + hq) * (size_t)a.Nq * D;
+  const float* kh = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
+  const float* vh = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
+
+  int kend = a.Nk;
+  if (CAUSAL) kend = min(a.Nk, min(qw0 + 32, a.Nq) - 1 + off + 1);
+  const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  // Q fragment s: row qi, dim 2s + h
+  float qf[D / 2];
+#pragma unroll
+  for (int s = 0; s < D / 2; s++) qf[s] = qi < a.Nq ? qh[(size_t)qi * D + 2 * s + h32] : 0.0f;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
+  float m_run = kNegInf, l_run = 0.0f;
+
+  for (int t = 0; t < n_tiles; t++) {
+    const int j0 = t * BN;
+    __syncthreads();
+    for (int e = lane; e < BN * D; e += 64) {
+      const int r = e / D, cc = e % D;
+      const bool in = j0 + r < a.Nk;
+      kt[r * LD + cc] = in ? kh[(size_t)(j0 + r) * D + cc] : 0.0f;
+      vt[r * LD + cc] = in ? vh[(size_t)(j0 + r) * D + cc] : 0.0f;
+    }
+    __syncthreads();
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 2; s++) st = mfma32_f32(kt[l32 * LD + 2 * s + h32], qf[s], st);
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int j = j0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      bool ok = j < a.Nk;
+      if (CAUSAL) ok = ok && (j <= qi + off);
+      if (!ok) st[r] = kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[r]);
+    mx = halves_max(mx) * a.c;
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new > m_run) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[cb][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      st[r] = fast_exp2(__builtin_fmaf(st[r], a.c, -m_use));
+      l_run += st[r];
+    }
+    // O^T += V^T P^T: MFMA r contracts over keys (8(r/4) + r%4) and (8(r/4) + 4 + r%4)
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int key = 8 * (r >> 2) + 4 * h32 + (r & 3);
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++) acc[cb] = mfma32_f32(vt[key * LD + cb * 32 + l32], st[r], acc[cb]);
+    }
+  }
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qi < a.Nq) {
+    float* orow = a.o + ((size_t)b * a.Hq + hq) * (size_t)a.Nq * D + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) orow[cb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3)] = acc[cb][r] * inv;
+    if (a.lse != nullptr && h32 == 0)
+      a.lse[((size_t)b * a.Hq + hq) * a.Nq + qi] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, int NW, int BN, bool CAUSAL>
+hipError_t launch_bf16(const FwdProblem& p, hipStream_t s) {
+  FwdArgs a;
+  a.q = (const __bf16*)p.q;
+  a.k = (const __bf16*)p.k;
+  a.v = (const __bf16*)p.v;
+  a.o = (__bf16*)p.o;
+  a.lse = p.lse;
+  a.B = (int)p.B;
+  a.Hq = (int)p.Hq;
+  a.Hkv = (int)p.Hkv;
+  a.Nq = (int)p.Nq;
+  a.Nk = (int)p.Nk;
+  a.g = a.Hq / a.Hkv;
+  a.n_qtiles = (a.Nq + NW * 32 - 1) / (NW * 32);
+  a.n_wgs = a.B * a.Hq * a.n_qtiles;
+  a.c = p.scale * kLog2e;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, CAUSAL>), dim3(a.n_wgs), dim3(NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32(const FwdProblem& p, hipStream_t s) {
+  FwdArgsF32 a;
+  a.q = (const float*)p.q;
+  a.k = (const float*)p.k;
+  a.v = (const float*)p.v;
+  a.o = (float*)p.o;
+  a.lse = p.lse;
+  a.B = (int)p.B;
+  a.Hq = (int)p.Hq;
+  a.Hkv = (int)p.Hkv;
+  a.Nq = (int)p.Nq;
+  a.Nk = (int)p.Nk;
+  a.g = a.Hq / a.Hkv;
+  a.n_qtiles = (a.Nq + 31) / 32;
+  a.n_wgs = a.B * a.Hq * a.n_qtiles;
+  a.c = p.scale * kLog2e;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(a.n_wgs), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
+  const bool causal = p.causal != 0;
+  if (p.bf16) {
+    if (p.d == 128) return causal ? launch_bf16<128, 4, 64, true>(p, s) : launch_bf16<128, 4, 64, false>(p, s);
+    return causal ? launch_bf16<64, 4, 64, true>(p, s) : launch_bf16<64, 4, 64, false>(p, s);
+  }
+  if (p.d == 128) return causal ? launch_f32<128, true>(p, s) : launch_f32<128, false>(p, s);
+  return causal ? launch_f32<64, true>(p, s) : launch_f32<64, false>(p, s);
+}
+
+}  // namespace attn

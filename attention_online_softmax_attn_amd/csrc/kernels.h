@@ -1,0 +1,59 @@
+// Internal interface between the C ABI (attn_abi.cpp) and the kernel files.
+// Arguments arrive here already validated: d in {64, 128}, Hq % Hkv == 0,
+// every size positive and at most ATTN_MAX_SEQ, pointers non-null where needed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int64_t B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  bool bf16;
+};
+hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
+
+struct DecodeProblem {
+  const void* q;  // [B, Hq, 1, d] bf16
+  const void* k;  // [B, Hkv, Nk, d] bf16
+  const void* v;
+  void* o;        // [B, Hq, 1, d] bf16
+  float* lse;     // [B, Hq] fp32, may be null
+  int64_t B, Hq, Hkv, Nk, d;
+  float scale;
+  int num_splits;  // >= 1, already resolved
+  int chunk;       // keys per split, a multiple of the kernel's key tile
+  float* part_acc; // [B, Hq, num_splits, d] fp32 (unused when num_splits == 1)
+  float* part_ml;  // [B, Hq, num_splits, 2] fp32 (running max in log2 units, sum)
+};
+// Keys per decode tile; split chunks are whole multiples of it.
+constexpr int kDecodeTile = 32;
+hipError_t launch_decode(const DecodeProblem& p, hipStream_t s);
+
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;  // workspace: [B, Hq, Nq] fp32
+  int64_t B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+};
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t s);
+
+}  // namespace attn

@@ -1,0 +1,309 @@
+"""Benchmark of the fused-attention hot path on one MI355X.
+
+One step is one pass over every path of the hot path, each at the shape its
+throughput target is stated for:
+  prefill   causal forward, B=1, Hq=32, Hkv=8, N=44032, d=128 (bf16 in, fp32 accumulate)
+  decode    split-KV decode, 48 streams, 32 q / 8 kv heads, d=128, 4096 keys each
+  backward  causal backward from the saved LSE, B=4, H=16, N=2048, d=128 (fp32 grads)
+Inputs are seeded synthetic N(0,1) tensors rounded to bf16 and are resident in
+HBM before the timed region.  The backward's O and LSE come from a forward run
+outside the timed region.
+
+value    = algorithmic attention TFLOP/s of the whole step
+           (fwd 4*B*Hq*Nq*Nk*d, bwd 10*B*Hq*Nq*Nk*d, both halved when causal;
+            decode 4*B*Hq*Nk*d)
+paths    = per-path time, TFLOP/s or GB/s, and fraction of the MI355X roofline
+roofline = the prefill forward kernel (the step's dominant kernel) against the
+           dense bf16 MFMA peak, timed with HIP events on its own stream
+cpu_baseline = the CPU oracle on a bounded sample of the same step's work
+
+Usage: python bench.py [--steps K] [--warmup W] [--no-cpu] [--paths fwd,decode,bwd]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "attention fwd/bwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak"
+
+PREFILL = dict(B=1, Hq=32, Hkv=8, N=44032, d=128, causal=True, seed=4)
+DECODE = dict(B=48, Hq=32, Hkv=8, L=4096, d=128, seed=3000 + 100 * 48 + 3)
+BACKWARD = dict(B=4, H=16, N=2048, d=128, causal=True, seed=5)
+
+
+def fwd_flops(B, Hq, Nq, Nk, d, causal):
+    return 4.0 * B * Hq * Nq * Nk * d * (0.5 if causal else 1.0)
+
+
+def bwd_flops(B, Hq, Nq, Nk, d, causal):
+    return 10.0 * B * Hq * Nq * Nk * d * (0.5 if causal else 1.0)
+
+
+def decode_bytes(B, Hq, Hkv, L, d):
+    return 2.0 * B * Hkv * L * d * 2 + 2.0 * B * Hq * d * 2 + B * Hq * 4
+
+
+def decode_flops(B, Hq, L, d):
+    return 4.0 * B * Hq * L * d
+
+
+def to_dev(x):
+    import numpy as np
+    import torch
+
+    import synth
+
+    bits = synth.round_bf16_bits(x)
+    return torch.from_numpy(bits.view(np.int16).reshape(x.shape)).view(torch.bfloat16).cuda()
+
+
+def setup(paths):
+    import synth
+
+    st = {}
+    if "fwd" in paths:
+        c = PREFILL
+        q, k, v = synth.attn_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["N"], c["N"], c["d"], bf16=True)
+        st["fwd_host"] = (q, k, v)
+        st["fwd"] = (to_dev(q), to_dev(k), to_dev(v))
+    if "decode" in paths:
+        c = DECODE
+        q, k, v = synth.attn_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], 1, c["L"], c["d"], bf16=True)
+        st["decode_host"] = (q, k, v)
+        st["decode"] = (to_dev(q), to_dev(k), to_dev(v))
+    if "bwd" in paths:
+        c = BACKWARD
+        q, k, v, do = synth.attn_inputs(c["seed"], c["B"], c["H"], c["H"], c["N"], c["N"], c["d"], bf16=True,
+                                        with_dout=True)
+        st["bwd_host"] = (q, k, v, do)
+        st["bwd"] = (to_dev(q), to_dev(k), to_dev(v), to_dev(do))
+    return st
+
+
+def run_gpu(paths, steps, warmup):
+    import torch
+
+    import attention_online_softmax_attn_amd as am
+
+    st = setup(paths)
+    dev_out = {}
+    # preallocated outputs and workspaces: the timed region only launches kernels
+    if "fwd" in paths:
+        q, k, v = st["fwd"]
+        dev_out["fwd"] = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"))
+    if "decode" in paths:
+        q, k, v = st["decode"]
+        c = DECODE
+        ws = am.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], 0)
+        dev_out["decode"] = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"),
+                             torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda"))
+    if "bwd" in paths:
+        q, k, v, do = st["bwd"]
+        c = BACKWARD
+        o, lse = am.attn_fwd(q, k, v, causal=True)
+        ws = am.bwd_workspace_bytes(c["B"], c["H"], c["N"], c["d"])
+        f32 = dict(dtype=torch.float32, device="cuda")
+        dev_out["bwd"] = (o, lse, torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32),
+                          torch.empty(ws, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+
+    def run_path(name):
+        if name == "fwd":
+            q, k, v = st["fwd"]
+            o, lse = dev_out["fwd"]
+            am.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+        elif name == "decode":
+            q, k, v = st["decode"]
+            o, lse, ws = dev_out["decode"]
+            am.attn_decode_splitkv(q, k, v, workspace=ws, out=o, lse=lse)
+        else:
+            q, k, v, do = st["bwd"]
+            o, lse, dq, dk, dv, ws = dev_out["bwd"]
+            am.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    order = [p for p in ("fwd", "decode", "bwd") if p in paths]
+    for _ in range(warmup):
+        for p in order:
+            run_path(p)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, p in enumerate(order):
+            run_path(p)
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {p: [] for p in order}
+    for s in range(steps):
+        for i, p in enumerate(order):
+            per[p].append(ev[s][i].elapsed_time(ev[s][i + 1]))
+    step_ms = [sum(per[p][s] for p in order) for s in range(steps)]
+    return st, per, step_ms, wall
+
+
+def cpu_baseline(st, paths, budget_s):
+    """The oracle, as it stands, on a bounded sample of the step's work."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    flops = 0.0
+    secs = 0.0
+    parts = []
+    share = budget_s / max(1, len(paths))
+    if "fwd" in paths:
+        c = PREFILL
+        q, k, v = st["fwd_host"]
+        rng_seed = 40004
+        n, done_rows = 64, 0
+        t_fwd = 0.0
+        while t_fwd < share:
+            rows = synth.sample_rows(rng_seed + done_rows, n, c["B"], c["Hq"], c["N"])
+            t = time.perf_counter()
+            oracle.fwd_rows(q, k, v, rows, 1.0 / math.sqrt(c["d"]), True)
+            t_fwd += time.perf_counter() - t
+            flops += float(np.sum(4.0 * c["d"] * (rows[:, 2] + 1)))
+            done_rows += n
+            n *= 2
+        secs += t_fwd
+        parts.append(f"{done_rows} random query rows of the N=44032 causal prefill")
+    if "decode" in paths:
+        c = DECODE
+        q, k, v = st["decode_host"]
+        t = time.perf_counter()
+        oracle.fwd(q, k, v, 1.0 / math.sqrt(c["d"]), False)
+        secs += time.perf_counter() - t
+        flops += decode_flops(c["B"], c["Hq"], c["L"], c["d"])
+        parts.append("the full 48x4096 decode")
+    if "bwd" in paths:
+        c = BACKWARD
+        q, k, v, do = st["bwd_host"]
+        nth = oracle.num_threads()
+        heads = 0
+        t_bwd = 0.0
+        while t_bwd < share and heads < c["B"] * c["H"]:
+            n = min(nth, c["B"] * c["H"] - heads)
+            sel = [(h // c["H"], h % c["H"]) for h in range(heads, heads + n)]
+            bs, hs = [x[0] for x in sel], [x[1] for x in sel]
+            sl = lambda x: np.ascontiguousarray(x[bs, hs][:, None])
+            t = time.perf_counter()
+            oracle.bwd(sl(q), sl(k), sl(v), sl(do), 1.0 / math.sqrt(c["d"]), True)
+            t_bwd += time.perf_counter() - t
+            flops += n * bwd_flops(1, 1, c["N"], c["N"], c["d"], True)
+            heads += n
+        secs += t_bwd
+        parts.append(f"the backward of {heads} of the 64 (batch, head) problems at N=2048")
+    return {
+        "value": round(flops / secs / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "; ".join(parts) + f" ({secs:.1f} s of fp64 CPU work)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--paths", default="fwd,decode,bwd")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    paths = [p for p in args.paths.split(",") if p]
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    st, per, step_ms, wall = run_gpu(paths, args.steps, args.warmup)
+
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    out_paths = {}
+    total_flops = 0.0
+    if "fwd" in paths:
+        c = PREFILL
+        f = fwd_flops(c["B"], c["Hq"], c["N"], c["N"], c["d"], True)
+        t = sum(per["fwd"]) / len(per["fwd"])
+        out_paths["prefill_fwd"] = {"ms": round(t, 4), "ms_median": round(med(per["fwd"]), 4),
+                                    "tflops": round(f / t / 1e9, 2), "frac_mfma": round(f / t / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                    "shape": "B=1 Hq=32 Hkv=8 N=44032 d=128 causal"}
+        total_flops += f
+    if "decode" in paths:
+        c = DECODE
+        b = decode_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"])
+        t = sum(per["decode"]) / len(per["decode"])
+        out_paths["decode"] = {"ms": round(t, 4), "ms_median": round(med(per["decode"]), 4),
+                               "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
+                               "shape": "48 streams, Hq=32 Hkv=8 d=128, 4096 keys"}
+        total_flops += decode_flops(c["B"], c["Hq"], c["L"], c["d"])
+    if "bwd" in paths:
+        c = BACKWARD
+        f = bwd_flops(c["B"], c["H"], c["N"], c["N"], c["d"], True)
+        t = sum(per["bwd"]) / len(per["bwd"])
+        out_paths["backward"] = {"ms": round(t, 4), "ms_median": round(med(per["bwd"]), 4),
+                                 "tflops": round(f / t / 1e9, 2), "frac_mfma": round(f / t / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                 "shape": "B=4 H=16 N=2048 d=128 causal"}
+        total_flops += f
+    ms_step = sum(step_ms) / len(step_ms)
+    value = total_flops / ms_step / 1e9
+
+    roofline = None
+    if "fwd" in paths:
+        c = PREFILL
+        f = fwd_flops(c["B"], c["Hq"], c["N"], c["N"], c["d"], True)
+        t = sum(per["fwd"]) / len(per["fwd"])
+        ach = f / t / 1e9
+        roofline = {"kernel": "fwd_bf16_kernel<128,4,64,causal>", "bound": "mfma", "achieved": round(ach, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None}
+    sane = all(v.get("frac_mfma", 0) <= 1.0 and v.get("frac_hbm", 0) <= 1.0 for v in out_paths.values())
+    wall_ms = wall * 1e3 / args.steps
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fused attention hot path: causal prefill fwd N=44032 (32q/8kv) + split-KV decode "
+                               "48x4096 (32q/8kv) + causal bwd B=4 H=16 N=2048", "d": 128,
+                   "paths": ",".join(paths)},
+        "paths": out_paths,
+        "roofline": roofline,
+        "timer_check": {"event_ms_per_step": round(ms_step, 4), "wall_ms_per_step": round(wall_ms, 4),
+                        "agree": abs(wall_ms - ms_step) <= 0.1 * ms_step + 0.05},
+        "sane": sane,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(st, paths, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

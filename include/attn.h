@@ -1,0 +1,110 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused softmax-attention library.
+ *
+ * Operation (all entry points):
+ *     O = softmax(scale * Q K^T + mask) V,   LSE_i = ln sum_j exp(scale * q_i . k_j)
+ * computed in one fused pass per query tile: the streaming softmax state
+ * (running max m, running sum l, accumulator acc) is a monoid, so key blocks
+ * and split-KV partials may be folded in any grouping.  Source: the page
+ * "Não escreva kernels, derive-os", section "Aprofundamento", first paragraph
+ * (flash attention from the online softmax seen as a monoid) and FAQ entry
+ * "O que o Tang propõe de diferente?" (fusion, flash attention and the
+ * backward obtained by rewriting); the page "Tang Project Derives GPU Kernels
+ * via IR ...", section "Details" (monoid reductions; causal forward passes;
+ * decode at 16-48 concurrent streams).  The pages print no formula: the
+ * definition above is the textbook softmax attention.
+ *
+ * Conventions shared by every entry point
+ *   Layout   q, o, dout, dq : [B, Hq,  Nq, d]  contiguous, d fastest
+ *            k, v, dk, dv   : [B, Hkv, Nk, d]  contiguous, d fastest
+ *            lse            : [B, Hq,  Nq]     fp32, natural log
+ *   Heads    query head h reads kv head h / (Hq / Hkv)  (grouped-query)
+ *   Causal   key j is visible to query i iff j <= i + (Nk - Nq)
+ *            (bottom-right alignment; a single decode query sees every key)
+ *   Empty    a query row with no visible key gets O = 0, LSE = -inf and
+ *            zero gradients
+ *   Types    dtype selects the element type of q, k, v, o and dout;
+ *            accumulation is fp32; lse and all gradients are fp32
+ *   Sizes    d must be 64 or 128; Hq % Hkv == 0; B, Nq, Nk >= 0; scale > 0
+ *            and finite; Nq, Nk <= ATTN_MAX_SEQ
+ *   Memory   every pointer is a device pointer owned by the caller; the
+ *            library never allocates, frees or synchronises.  Inputs are
+ *            read only; outputs are fully overwritten.  Workspaces are
+ *            caller-provided scratch sized by the *_workspace_bytes calls.
+ *   Streams  stream is a hipStream_t (NULL = the default stream); each call
+ *            enqueues its kernels on it and returns without waiting.
+ *   Errors   every argument check runs on the host before any HIP call and
+ *            returns a status; a failed launch returns ATTN_ERR_HIP.  Device
+ *            faults surface at the caller's next synchronisation.  NaN or
+ *            Inf inputs propagate and are not checked.  A call whose outputs
+ *            are empty (B, Hq or Nq zero) returns ATTN_OK and launches nothing.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_MAX_SEQ (1 << 24)
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,     /* null pointer, negative size, Hq % Hkv != 0, bad scale or dtype */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64,128}, size above ATTN_MAX_SEQ, dtype */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than required */
+  ATTN_ERR_HIP = 4          /* a kernel launch failed */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/*
+ * Forward prefill.  q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] -> o [B,Hq,Nq,d] (dtype),
+ * lse [B,Hq,Nq] fp32 (may be NULL when not needed).  dtype ATTN_BF16 runs the
+ * contractions on bf16 MFMA; ATTN_F32 on fp32 MFMA.  Causal key blocks that
+ * no query of a tile can see are neither loaded nor computed.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, attn_dtype dtype,
+                     void* stream);
+
+/*
+ * Split-KV decode: one query token per stream (Nq must be 1) against a KV
+ * history of Nk keys.  Each kv head's keys are cut into num_splits chunks
+ * (0 = automatic plan); every chunk yields a partial state (m, l, acc) for the
+ * Hq/Hkv query heads that share the kv head, written to the workspace, and a
+ * merge kernel folds the partials with the monoid rule and writes o (dtype)
+ * and lse (fp32, may be NULL).  Only ATTN_BF16 is built.  causal is accepted
+ * and has no effect (a single bottom-right-aligned query sees every key).
+ */
+int attn_decode_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d);
+size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits);
+attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                                int num_splits, void* workspace, size_t workspace_bytes, attn_dtype dtype,
+                                void* stream);
+
+/*
+ * Backward from the saved log-sum-exp.  Inputs q, k, v, o, dout (dtype) and
+ * lse (fp32, as written by attn_fwd with the same arguments); outputs dq
+ * [B,Hq,Nq,d], dk and dv [B,Hkv,Nk,d], all fp32 and fully overwritten (dk and
+ * dv sum over the query heads that share a kv head).  The workspace holds the
+ * per-row statistic D_i = dO_i . O_i.  Only ATTN_BF16 is built.
+ */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d);
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     float* dq, float* dk, float* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                     int64_t d, float scale, int causal, void* workspace, size_t workspace_bytes, attn_dtype dtype,
+                     void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* attn_strerror(attn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

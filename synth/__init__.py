@@ -49,12 +49,22 @@ def normal(seed: int, shapes, bf16: bool, scale: float = 1.0):
 
 
 def attn_inputs(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, bf16: bool, with_dout: bool = False,
-                scale: float = 1.0):
-    """Q [B,Hq,Nq,d], K, V [B,Hkv,Nk,d] (and dO [B,Hq,Nq,d]) drawn in that order."""
+                scale: float = 1.0, qk_scale: float = 1.0):
+    """Q [B,Hq,Nq,d], K, V [B,Hkv,Nk,d] (and dO [B,Hq,Nq,d]) drawn in that order.
+
+    ``scale`` multiplies every tensor; ``qk_scale`` multiplies Q and K only
+    (before rounding), which sharpens the softmax without enlarging V or dO.
+    """
     shapes = [(B, Hq, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d)]
     if with_dout:
         shapes.append((B, Hq, Nq, d))
-    return normal(seed, shapes, bf16, scale)
+    out = normal(seed, shapes, False, scale)
+    if qk_scale != 1.0:
+        out[0] = (out[0] * np.float32(qk_scale)).astype(np.float32)
+        out[1] = (out[1] * np.float32(qk_scale)).astype(np.float32)
+    if bf16:
+        out = [bf16_bits_to_f32(round_bf16_bits(x)).reshape(x.shape) for x in out]
+    return out
 
 
 def sample_rows(seed: int, n: int, B: int, Hq: int, Nq: int, forced_i=()) -> np.ndarray:

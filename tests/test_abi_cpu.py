@@ -1,0 +1,157 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments on the host before any HIP call.  No compute runs."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_online_softmax_attn_amd as am
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(attn_[a-z0-9_]+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_decode_splitkv", "attn_bwd", "attn_decode_workspace_bytes",
+              "attn_bwd_workspace_bytes", "attn_decode_num_splits", "attn_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = am.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in include/attn.h but not exported"
+    out = os.popen(f"nm -D --defined-only {am.LIB_PATH}").read()
+    for n in declared_functions():
+        assert re.search(rf"\bT {n}$", out, re.M), f"{n} is not a defined dynamic symbol"
+
+
+def test_library_targets_gfx950():
+    data = open(am.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_strerror():
+    assert am.strerror(am.ATTN_OK) == "ok"
+    assert "workspace" in am.strerror(am.ATTN_ERR_WORKSPACE)
+    assert am.strerror(99) == "unknown status"
+
+
+# Fake device pointers are only used for calls that must be rejected on the
+# host.  They are never passed where a GPU is visible.
+no_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.device_count() > 0, reason="host-only rejection tests use fake pointers"
+)
+P = ctypes.c_void_p(0x100000)
+NUL = None
+
+
+def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.125, causal=0, dt=am.ATTN_BF16):
+    return am.lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dt, None)
+
+
+@no_gpu
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(q=NUL), am.ATTN_ERR_INVALID),
+        (dict(o=NUL), am.ATTN_ERR_INVALID),
+        (dict(k=NUL), am.ATTN_ERR_INVALID),
+        (dict(B=-1), am.ATTN_ERR_INVALID),
+        (dict(Hq=3, Hkv=2), am.ATTN_ERR_INVALID),
+        (dict(Hkv=0), am.ATTN_ERR_INVALID),
+        (dict(Nq=-2), am.ATTN_ERR_INVALID),
+        (dict(scale=0.0), am.ATTN_ERR_INVALID),
+        (dict(scale=-1.0), am.ATTN_ERR_INVALID),
+        (dict(scale=float("nan")), am.ATTN_ERR_INVALID),
+        (dict(scale=float("inf")), am.ATTN_ERR_INVALID),
+        (dict(dt=7), am.ATTN_ERR_INVALID),
+        (dict(d=96), am.ATTN_ERR_UNSUPPORTED),
+        (dict(d=256), am.ATTN_ERR_UNSUPPORTED),
+        (dict(Nk=(1 << 24) + 1), am.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+@no_gpu
+def test_empty_outputs_launch_nothing():
+    # B = 0 or Nq = 0: nothing to write, accepted even with null pointers
+    assert fwd(q=NUL, k=NUL, v=NUL, o=NUL, lse=NUL, B=0) == am.ATTN_OK
+    assert fwd(q=NUL, k=NUL, v=NUL, o=NUL, lse=NUL, Nq=0) == am.ATTN_OK
+
+
+def dec(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scale=0.088, splits=0, ws=P,
+        ws_bytes=1 << 30, dt=am.ATTN_BF16):
+    return am.lib().attn_decode_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, 0, splits, ws, ws_bytes, dt,
+                                        None)
+
+
+@no_gpu
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(Nq=2), am.ATTN_ERR_INVALID),
+        (dict(splits=-1), am.ATTN_ERR_INVALID),
+        (dict(q=NUL), am.ATTN_ERR_INVALID),
+        (dict(dt=am.ATTN_F32), am.ATTN_ERR_UNSUPPORTED),
+        (dict(Hq=64, Hkv=1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(ws=NUL), am.ATTN_ERR_WORKSPACE),
+        (dict(ws_bytes=16), am.ATTN_ERR_WORKSPACE),
+        (dict(d=80), am.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_decode_rejects(kw, code):
+    assert dec(**kw) == code
+
+
+def test_split_plan_and_workspace():
+    n = am.decode_num_splits
+    # grouped-query decode at 32 q / 8 kv heads, d = 128
+    for B, L in [(1, 512), (1, 4096), (16, 4096), (48, 2048), (48, 4096)]:
+        s = n(B, 32, 8, L, 128)
+        assert 1 <= s <= max(1, L // 32)
+        ws = am.decode_workspace_bytes(B, 32, 8, L, 128, 0)
+        if s == 1:
+            assert ws == 0
+        else:
+            assert ws >= B * 32 * s * (128 + 2) * 4
+    # workgroup count B*Hkv*splits fills the 256 CUs in whole waves where it can
+    assert (48 * 8 * n(48, 32, 8, 4096, 128)) % 256 == 0
+    assert (16 * 8 * n(16, 32, 8, 4096, 128)) % 256 == 0
+    # explicit split counts are honoured up to one split per 32-key tile
+    assert am.decode_workspace_bytes(1, 4, 1, 100, 64, 7) == am.decode_workspace_bytes(1, 4, 1, 100, 64, 4)
+    assert am.decode_workspace_bytes(1, 4, 1, 0, 64, 0) == 0
+    assert am.bwd_workspace_bytes(4, 16, 2048, 128) >= 4 * 16 * 2048 * 4
+
+
+def bwd(ws=P, ws_bytes=1 << 30, dt=am.ATTN_BF16, d=128, lse=P, Hq=4, Hkv=2):
+    return am.lib().attn_bwd(P, P, P, P, P, lse, P, P, P, 1, Hq, Hkv, 64, 64, d, 0.1, 1, ws, ws_bytes, dt, None)
+
+
+@no_gpu
+def test_bwd_rejects():
+    assert bwd(ws=NUL) == am.ATTN_ERR_WORKSPACE
+    assert bwd(ws_bytes=4) == am.ATTN_ERR_WORKSPACE
+    assert bwd(dt=am.ATTN_F32) == am.ATTN_ERR_UNSUPPORTED
+    assert bwd(d=32) == am.ATTN_ERR_UNSUPPORTED
+    assert bwd(lse=NUL) == am.ATTN_ERR_INVALID
+    assert bwd(Hq=3) == am.ATTN_ERR_INVALID
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        am.attn_fwd(q, q, q)

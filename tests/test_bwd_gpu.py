@@ -1,0 +1,107 @@
+"""Backward on the GPU against the analytic fp64 CPU oracle.  The GPU backward
+takes the GPU forward's O and LSE (as a caller would); the oracle recomputes
+everything from Q, K, V and dO alone."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_online_softmax_attn_amd as am
+import synth
+from gpu_helpers import TOL_GRAD, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_grads(q, k, v, do, causal, scale):
+    qd, kd, vd, dod = dev(q, True), dev(k, True), dev(v, True), dev(do, True)
+    o, lse = am.attn_fwd(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = am.attn_bwd(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv)
+
+
+def run_case(oracle_mod, seed, B, Hq, Hkv, Nq, Nk, d, causal, peak=1.0, rel=None):
+    print(f"bwd case seed={seed} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = synth.attn_inputs(seed, B, Hq, Hkv, Nq, Nk, d, bf16=True, with_dout=True, qk_scale=peak)
+    gq, gk, gv = gpu_grads(q, k, v, do, causal, scale)
+    eq, ek, ev = oracle_mod.bwd(q, k, v, do, scale, causal)
+    errs = []
+    for name, g, e in (("dQ", gq, eq), ("dK", gk, ek), ("dV", gv, ev)):
+        tol = TOL_GRAD if rel is None else rel * float(np.abs(e).max())
+        errs.append(assert_close(name, g, e, tol))
+    print("  max-abs dQ {:.3e} dK {:.3e} dV {:.3e}".format(*errs), flush=True)
+
+
+SHAPES = [
+    # B, Hq, Hkv, Nq, Nk, d
+    (1, 1, 1, 17, 17, 128),
+    (2, 2, 2, 64, 64, 64),
+    (1, 4, 2, 129, 129, 128),
+    (1, 4, 1, 300, 300, 64),
+    (1, 2, 2, 100, 260, 128),   # Nq < Nk
+    (1, 2, 1, 260, 100, 128),   # Nq > Nk: rows with no visible key (causal)
+    (2, 8, 2, 512, 512, 128),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_shapes(oracle_mod, shape, causal):
+    B, Hq, Hkv, Nq, Nk, d = shape
+    run_case(oracle_mod, 5000 + Nq + 3 * Nk + d, B, Hq, Hkv, Nq, Nk, d, causal)
+
+
+def test_bwd_peaked(oracle_mod):
+    # Q and K scaled by 2: gradients grow ~3x over the N(0,1) case, and the
+    # bf16 operands (P, dS) bound the error relative to that magnitude.  At
+    # N(0,1) the 5e-2 tolerance is ~2% of max|gradient|; the same 2% is held here.
+    run_case(oracle_mod, 5100, 1, 2, 1, 200, 200, 128, True, peak=2.0, rel=0.02)
+
+
+def test_bwd_zero_dout_gives_zero():
+    q, k, v, _ = synth.attn_inputs(5200, 1, 4, 2, 100, 100, 128, bf16=True, with_dout=True)
+    qd, kd, vd = dev(q, True), dev(k, True), dev(v, True)
+    o, lse = am.attn_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = am.attn_bwd(qd, kd, vd, o, torch.zeros_like(o), lse, causal=True)
+    torch.cuda.synchronize()
+    for g in (dq, dk, dv):
+        assert torch.all(g == 0)
+
+
+def test_bwd_repeatable_bitwise():
+    q, k, v, do = synth.attn_inputs(5300, 1, 4, 2, 300, 300, 128, bf16=True, with_dout=True)
+    qd, kd, vd, dod = dev(q, True), dev(k, True), dev(v, True), dev(do, True)
+    o, lse = am.attn_fwd(qd, kd, vd, causal=True)
+    a = am.attn_bwd(qd, kd, vd, o, dod, lse, causal=True)
+    b = am.attn_bwd(qd, kd, vd, o, dod, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------- full size: B=4, H=16, N=2048, d=128, causal
+
+
+def test_c5_full_size_sampled_heads(oracle_mod):
+    B, H, N, d = 4, 16, 2048, 128
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = synth.attn_inputs(5, B, H, H, N, N, d, bf16=True, with_dout=True)
+    print("C5 bwd: launching", flush=True)
+    gq, gk, gv = gpu_grads(q, k, v, do, True, scale)
+    # every (b, h) is an independent problem: check four sampled heads in full
+    rng = np.random.default_rng(50005)
+    picks = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(2)]
+    bs = [p[0] for p in picks]
+    hs = [p[1] for p in picks]
+    sl = lambda x: np.ascontiguousarray(x[bs, hs][:, None])  # [4, 1, N, d]
+    eq, ek, ev = oracle_mod.bwd(sl(q), sl(k), sl(v), sl(do), scale, True)
+    assert_close("dQ", gq[bs, hs], eq[:, 0], TOL_GRAD)
+    assert_close("dK", gk[bs, hs], ek[:, 0], TOL_GRAD)
+    assert_close("dV", gv[bs, hs], ev[:, 0], TOL_GRAD)
+    # invariants over every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
+    assert np.max(np.abs(gk.sum(axis=2))) <= 0.5, np.max(np.abs(gk.sum(axis=2)))
+    sdo = do.astype(np.float64).sum(axis=2)
+    assert np.max(np.abs(gv.sum(axis=2) - sdo)) <= 0.5
