@@ -40,6 +40,38 @@ DECODE = dict(B=48, Hq=32, Hkv=8, L=4096, d=128, seed=3000 + 100 * 48 + 3)
 BACKWARD = dict(B=4, H=16, N=2048, d=128, causal=True, seed=5)
 
 
+CSRC = os.path.join(ROOT, "attention_online_softmax_attn_amd", "csrc")
+FWD_COUNTERS = os.path.join(ROOT, "profiles", "fwd_bf16_prefill_n44032_hbm_counters.md")
+
+
+def counted_traffic(summary_path):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel sources have changed since the counters were taken."""
+    import hashlib
+
+    try:
+        text = open(summary_path).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        line = line.strip()
+        for key in ("source_files:", "source_sha256:", "traffic_bytes_per_launch:"):
+            if line.startswith(key):
+                fields[key[:-1]] = line[len(key):].strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for name in fields["source_files"].split():
+        try:
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+        except OSError:
+            return None
+    if h.hexdigest() != fields["source_sha256"]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def fwd_flops(B, Hq, Nq, Nk, d, causal):
     return 4.0 * B * Hq * Nq * Nk * d * (0.5 if causal else 1.0)
 
@@ -216,6 +248,21 @@ def cpu_baseline(st, paths, budget_s):
     }
 
 
+def copy_probe(mib):
+    """A plain device copy of known size: the HBM byte counters of this one
+    dispatch (read and written bytes = mib MiB each) calibrate the counters
+    taken on the attention kernels."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "copy_probe_kib": n * 4 // 1024}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +271,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--paths", default="fwd,decode,bwd")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -235,6 +284,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+        return
     st, per, step_ms, wall = run_gpu(paths, args.steps, args.warmup)
 
     med = lambda xs: sorted(xs)[len(xs) // 2]
@@ -275,7 +327,7 @@ def main():
         ach = f / t / 1e9
         roofline = {"kernel": "fwd_bf16_kernel<128,4,64,causal>", "bound": "mfma", "achieved": round(ach, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                    "traffic": None}
+                    "traffic": counted_traffic(FWD_COUNTERS)}
     sane = all(v.get("frac_mfma", 0) <= 1.0 and v.get("frac_hbm", 0) <= 1.0 for v in out_paths.values())
     wall_ms = wall * 1e3 / args.steps
     line = {
