@@ -31,30 +31,44 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    out = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+# Per-source scheduling: the backward kernels run one wave per SIMD, so their
+# LDS operand reads must be issued well ahead of the MFMAs that use them and the
+# exponentials interleaved with independent MFMAs; the ILP-maximising machine
+# scheduler does that, the default (occupancy-driven) one sinks every read next
+# to its use.
+SOURCE_FLAGS = {
+    "bwd_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
+def _compile(src: str, objdir: str = OBJDIR, defines=()) -> str:
+    os.makedirs(objdir, exist_ok=True)
+    out = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", out]
+    extra = SOURCE_FLAGS.get(src, [])
+    cmd = [HIPCC, *FLAGS, *extra, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library.  Always rebuilds."""
+def build(verbose: bool = False, lib: str = LIB, objdir: str = OBJDIR, defines=()) -> str:
+    """Compile every source for gfx950 and link the shared library.  Always rebuilds.
+
+    ``defines`` (NAME=VALUE strings) override the kernels' compile-time tile
+    choices; the default library is built without any."""
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, objdir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

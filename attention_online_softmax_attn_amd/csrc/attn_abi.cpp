@@ -153,7 +153,7 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d) {
   if (B < 0 || Hq < 1 || Nq < 0 || (d != 64 && d != 128)) return 0;
-  return align256((size_t)B * Hq * Nq * sizeof(float));
+  return align256((size_t)B * Hq * attn::bwd_record_rows(Nq) * 2 * sizeof(float));
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -178,7 +178,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.delta = (float*)workspace;
+  p.stats = (float*)workspace;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -13,10 +13,12 @@
 // gradients.
 //
 // Three kernels, no atomics (every output element has one writer):
-//   bwd_pre   D_i = dO_i . O_i                              (one pass over O, dO)
+//   bwd_pre   per query row: (LSE * log2 e, D_i = dO_i . O_i) into the
+//             workspace, one 8-byte record per row
 //   bwd_dkdv  workgroup = (b, kv head, 32*NW keys).  K and V fragments stay in
 //             registers; for every query head of the group and every query
-//             tile that can see the keys, Q and dO stream through LDS.
+//             tile that can see the keys, Q, dO and the row records stream
+//             through LDS (double-buffered, direct-to-LDS loads).
 //             S = Q K^T and dP = dO V^T put keys on the MFMA N dimension, so
 //             P and dS come out with one key per lane and feed
 //             dV += P^T dO and dK += dS^T Q straight from registers, with dO
@@ -24,6 +26,12 @@
 //   bwd_dq    workgroup = (b, query head, 32*NW queries), the forward's
 //             layout: S^T = K Q^T and dP^T = V dO^T keep one query per lane;
 //             dQ^T += K^T dS^T reads K transposed from LDS.
+//
+// Both main kernels run one wave per SIMD (their live fragments and
+// accumulators exceed half the register file), so the softmax-gradient VALU
+// work is overlapped with MFMA work inside each wave: the loop over 32-row
+// (or 32-key) blocks is software-pipelined so that the contractions of block
+// i+1 are independent of, and issued around, the exponentials of block i.
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -41,14 +49,19 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;
+  float* stats;  // [B, Hq, nq_pad] x (LSE * log2 e, D)
   int B, Hq, Hkv, Nq, Nk, g;
+  int nq_pad;    // record rows per head: Nq rounded up to 128, so that the
+                 // 16-byte loads of records never straddle the end of a head
   int n_tiles, n_wgs;
   float c;      // scale * log2(e)
   float scale;
 };
 
-// D_i = dO_i . O_i: 16 lanes per row, 8 elements per lane (d = 128) or 4 (d = 64)
+// Row record: (LSE in log2 units, D_i).  A row with no visible key has
+// LSE = -inf; its record holds +inf so that every P of the row is 0.
+// 16 lanes per row, D/16 elements per lane.  Records of padding rows
+// (Nq <= i < nq_pad) are never written and never used unmasked.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int EPL = D / 16;
@@ -64,17 +77,27 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int w = 8; w >= 1; w >>= 1) s += __shfl_xor(s, w, 16);
-  if (row < rows && sub == 0) a.delta[row] = s;
+  if (row < rows && sub == 0) {
+    const float l = a.lse[row];
+    const size_t rec = (size_t)(row / a.Nq) * a.nq_pad + row % a.Nq;
+    a.stats[2 * rec + 0] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+    a.stats[2 * rec + 1] = s;
+  }
 }
 
-template <int D, int NW, bool CAUSAL>
+// ---------------------------------------------------------------------------
+// dK, dV.  Each wave owns 32 keys; a query tile of BQ rows is processed in
+// 32-row blocks.
+template <int D, int NW, int BQ, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BQ = 32;                 // queries per tile
-  constexpr int TILE = BQ * D * 2;       // bytes of one Q or dO tile
+  constexpr int TILE = BQ * D * 2;  // bytes of one Q or dO tile
+  constexpr int STAGE = 2 * TILE + 1024;  // Q, dO, row records (BQ * 8 <= 1024 bytes)
   constexpr int CPR = D / 8;
   constexpr int LOADS = BQ * CPR / (64 * NW);
+  constexpr int NB = BQ / 32;  // 32-row blocks per tile
   static_assert(LOADS * 64 * NW == BQ * CPR, "tile must split evenly");
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // [Q0 | dO0 | Q1 | dO1]
+  static_assert(BQ % 32 == 0 && BQ * 8 <= 1024, "BQ must be 32, 64, 96 or 128");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];  // [Q0 | dO0 | R0 | Q1 | dO1 | R1]
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -122,12 +145,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto head_of = [&](int it) { return kvh * a.g + it / per_head; };
   auto qtile_of = [&](int it) { return qt_first + it % per_head; };
 
-  auto issue = [&](int it, char* qt_l, char* dt_l) {
+  auto issue = [&](int it, char* st_l) {
     const int hq = head_of(it);
     const int i0 = qtile_of(it) * BQ;
-    const size_t q_head = ((size_t)b * a.Hq + hq) * (size_t)a.Nq * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_head, (uint32_t)a.Nq * D * 2);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + q_head, (uint32_t)a.Nq * D * 2);
+    const size_t q_row0 = ((size_t)b * a.Hq + hq) * (size_t)a.Nq;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_row0 * D, (uint32_t)a.Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + q_row0 * D, (uint32_t)a.Nq * D * 2);
 #pragma unroll
     for (int n = 0; n < LOADS; n++) {
       const int slab = n * NW + wave;
@@ -135,88 +158,139 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int r = p / CPR;
       const int cc = (p % CPR) ^ swz<D>(r);
       const uint32_t src = (uint32_t)(((i0 + r) * D + cc * 8) * 2);
-      buf_load_lds16(rq, src, (lds_void*)(qt_l + slab * 1024));
-      buf_load_lds16(rd, src, (lds_void*)(dt_l + slab * 1024));
+      buf_load_lds16(rq, src, (lds_void*)(st_l + slab * 1024));
+      buf_load_lds16(rd, src, (lds_void*)(st_l + TILE + slab * 1024));
+    }
+    if (wave == NW - 1) {
+      // row records of rows i0 .. i0 + 127 (the first BQ are used); rows past
+      // nq_pad read as zeros, rows past Nq are masked
+      const size_t rec0 = ((size_t)b * a.Hq + hq) * (size_t)a.nq_pad;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stats + 2 * rec0, (uint32_t)a.nq_pad * 8);
+      buf_load_lds16(rs, (uint32_t)(i0 * 8 + lane * 16), (lds_void*)(st_l + 2 * TILE));
     }
   };
 
-  auto compute = [&](int it, const char* qt_l, const char* dt_l) {
-    const int hq = head_of(it);
-    const int i0 = qtile_of(it) * BQ;
-    if (CAUSAL && i0 + BQ - 1 + off < jw) return;  // no query of the tile sees this wave's keys
-    const bool need_mask = (i0 + BQ > a.Nq) || (jw + 32 > a.Nk) || (CAUSAL && i0 + off < jw + 31);
-    // per-row statistics for rows 8(r/4) + 4h + r%4: LSE (log2 units) and D
-    const size_t rbase = ((size_t)b * a.Hq + hq) * a.Nq;
-    float l2[16], dd[16];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) {
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int i = i0 + 8 * r4 + 4 * h32 + e;
-        const bool in = i < a.Nq;
-        l2[4 * r4 + e] = in ? a.lse[rbase + i] * kLog2e : 0.0f;
-        dd[4 * r4 + e] = in ? a.delta[rbase + i] : 0.0f;
-      }
-    }
-    // S = Q K^T and dP = dO V^T (queries are M, this wave's keys are N)
-    f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+  // S and dP of 32-row block nb: queries on M (row 32 nb + l32 of the tile), keys on N.
+  // All operand fragments are read from LDS before the contractions start, so
+  // the MFMAs issue back to back instead of each waiting for its own read.
+  auto sdp = [&](const char* st_l, int nb, f32x16& sa, f32x16& da) {
+    const char* qt_l = st_l;
+    const char* dt_l = st_l + TILE;
+    bf16x8 qa[D / 16], oa[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; s++) {
-      const int off_b = l32 * (D * 2) + (((2 * s + h32) ^ swl) << 4);
-      const bf16x8 qa = *(const bf16x8*)(qt_l + off_b);
-      const bf16x8 da = *(const bf16x8*)(dt_l + off_b);
-      s_acc = mfma32(qa, kf[s], s_acc);
-      dp_acc = mfma32(da, vf[s], dp_acc);
+      const int off_b = (32 * nb + l32) * (D * 2) + (((2 * s + h32) ^ swl) << 4);
+      qa[s] = *(const bf16x8*)(qt_l + off_b);
+      oa[s] = *(const bf16x8*)(dt_l + off_b);
     }
-    // P and dS (P = 0 where the key is not visible, the row is padding, or the key is past Nk)
+    sa = f32x16{};
+    da = f32x16{};
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      float p = fast_exp2(__builtin_fmaf(s_acc[r], a.c, -l2[r]));
-      if (need_mask) {
-        const int i = i0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-        bool ok = (i < a.Nq) && (jl < a.Nk);
-        if (CAUSAL) ok = ok && (jl <= i + off);
-        if (!ok) p = 0.0f;
-      }
-      s_acc[r] = p;
-      dp_acc[r] = p * (dp_acc[r] - dd[r]);
+    for (int s = 0; s < D / 16; s++) {
+      sa = mfma32(qa[s], kf[s], sa);
+      da = mfma32(oa[s], vf[s], da);
     }
-    // dV += P^T dO, dK += dS^T Q: 16 queries per MFMA, dO and Q read transposed
+  };
+
+  // P = 2^(s c - LSE2) and dS = P (dP - D) in place; rows 8(r/4) + 4h + r%4 of block nb
+  auto pds = [&](const char* st_l, int nb, int i0, bool mask, f32x16& sa, f32x16& da) {
+    const float* rec = (const float*)(st_l + 2 * TILE);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+      const int rl = 32 * nb + 8 * r4 + 4 * h32;  // first of 4 consecutive rows
+      const f32x4 x0 = *(const f32x4*)(rec + 2 * rl);
+      const f32x4 x1 = *(const f32x4*)(rec + 2 * rl + 4);
+      const float l2[4] = {x0[0], x0[2], x1[0], x1[2]};
+      const float dd[4] = {x0[1], x0[3], x1[1], x1[3]};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int r = 4 * r4 + e;
+        float p = fast_exp2(__builtin_fmaf(sa[r], a.c, -l2[e]));
+        float ds = p * (da[r] - dd[e]);
+        if (mask) {
+          // selects, not products: a padding row's record may hold anything
+          const int i = i0 + rl + e;
+          bool ok = (i < a.Nq) && (jl < a.Nk);
+          if (CAUSAL) ok = ok && (jl <= i + off);
+          p = ok ? p : 0.0f;
+          ds = ok ? ds : 0.0f;
+        }
+        sa[r] = p;
+        da[r] = ds;
+      }
+    }
+  };
+
+  // dV += P^T dO, dK += dS^T Q over the 32 rows of block nb (dO and Q read
+  // transposed; all fragments of a 16-row half are read before its MFMAs)
+  auto dvdk = [&](const char* st_l, int nb, const f32x16& sa, const f32x16& da) {
+    const char* qt_l = st_l;
+    const char* dt_l = st_l + TILE;
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-      bf16x8 pa, sa;
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        pa[e] = to_bf16(s_acc[8 * hf + e]);
-        sa[e] = to_bf16(dp_acc[8 * hf + e]);
-      }
-      const int tr = 16 * hf + 4 * h32 + ((lane & 15) >> 2);
+      const int tr = 32 * nb + 16 * hf + 4 * h32 + ((lane & 15) >> 2);
+      bf16x8 dob[D / 32], qb[D / 32];
 #pragma unroll
       for (int cb = 0; cb < D / 32; cb++) {
         const int tc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         const int o1 = tile_off<D>(tr, tc), o2 = tile_off<D>(tr + 8, tc);
-        const bf16x8 dob = join_bf16(ds_read_tr16(dt_l + o1), ds_read_tr16(dt_l + o2));
-        const bf16x8 qb = join_bf16(ds_read_tr16(qt_l + o1), ds_read_tr16(qt_l + o2));
-        dv_acc[cb] = mfma32(pa, dob, dv_acc[cb]);
-        dk_acc[cb] = mfma32(sa, qb, dk_acc[cb]);
+        dob[cb] = join_bf16(ds_read_tr16(dt_l + o1), ds_read_tr16(dt_l + o2));
+        qb[cb] = join_bf16(ds_read_tr16(qt_l + o1), ds_read_tr16(qt_l + o2));
+      }
+      bf16x8 pa, sb;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        pa[e] = to_bf16(sa[8 * hf + e]);
+        sb[e] = to_bf16(da[8 * hf + e]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++) {
+        dv_acc[cb] = mfma32(pa, dob[cb], dv_acc[cb]);
+        dk_acc[cb] = mfma32(sb, qb[cb], dk_acc[cb]);
       }
     }
   };
 
-  auto step = [&](int it, const char* __restrict__ qc, const char* __restrict__ dc, char* __restrict__ qn,
-                  char* __restrict__ dn) {
+  auto compute = [&](int it, const char* st_l) {
+    const int i0 = qtile_of(it) * BQ;
+    if (CAUSAL && i0 + BQ - 1 + off < jw) return;  // no query of the tile sees this wave's keys
+    const bool need_mask = (i0 + BQ > a.Nq) || (jw + 32 > a.Nk) || (CAUSAL && i0 + off < jw + 31);
+    if (!need_mask) {
+      // software pipeline over the 32-row blocks: the S/dP contractions of
+      // block nb + 1 are issued before the P/dS arithmetic of block nb
+      f32x16 sa[2], da[2];
+      sdp(st_l, 0, sa[0], da[0]);
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) {
+        if (nb + 1 < NB) sdp(st_l, nb + 1, sa[(nb + 1) & 1], da[(nb + 1) & 1]);
+        pds(st_l, nb, i0, false, sa[nb & 1], da[nb & 1]);
+        dvdk(st_l, nb, sa[nb & 1], da[nb & 1]);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) {
+        if (CAUSAL && i0 + 32 * nb + 31 + off < jw) continue;
+        f32x16 sa, da;
+        sdp(st_l, nb, sa, da);
+        pds(st_l, nb, i0, true, sa, da);
+        dvdk(st_l, nb, sa, da);
+      }
+    }
+  };
+
+  auto step = [&](int it, const char* __restrict__ cur, char* __restrict__ nxt) {
     wait_vmem();
     __syncthreads();
-    if (it + 1 < n_iter) issue(it + 1, qn, dn);
-    compute(it, qc, dc);
+    if (it + 1 < n_iter) issue(it + 1, nxt);
+    compute(it, cur);
   };
-  char* const b0 = smem;
-  char* const b1 = smem + 2 * TILE;
-  if (n_iter > 0) issue(0, b0, b0 + TILE);
+  char* const s0 = smem;
+  char* const s1 = smem + STAGE;
+  if (n_iter > 0) issue(0, s0);
   for (int it = 0; it < n_iter; it += 2) {
-    step(it, b0, b0 + TILE, b1, b1 + TILE);
+    step(it, s0, s1);
     if (it + 1 >= n_iter) break;
-    step(it + 1, b1, b1 + TILE, b0, b0 + TILE);
+    step(it + 1, s1, s0);
   }
 
   // dV, dK accumulators: lane holds dim cb*32 + l32 of keys jw + 8(r/4) + 4h + r%4
@@ -235,12 +309,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
-template <int D, int NW, bool CAUSAL>
+// ---------------------------------------------------------------------------
+// dQ.  Each wave owns 32 query rows; key tiles of BN keys stream through LDS
+// and are processed in 32-key blocks.
+template <int D, int NW, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BN = 64;
   constexpr int TILE = BN * D * 2;
   constexpr int CPR = D / 8;
   constexpr int LOADS = BN * CPR / (64 * NW);
+  constexpr int KB = BN / 32;
   static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly");
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // [K0 | V0 | K1 | V1]
 
@@ -262,10 +339,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
   const int qi = qw0 + l32;
   const int off = a.Nk - a.Nq;
 
-  const size_t q_head = ((size_t)b * a.Hq + hq) * (size_t)a.Nq * D;
+  const size_t q_row0 = ((size_t)b * a.Hq + hq) * (size_t)a.Nq;
   const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_head, (uint32_t)a.Nq * D * 2);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + q_head, (uint32_t)a.Nq * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_row0 * D, (uint32_t)a.Nq * D * 2);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + q_row0 * D, (uint32_t)a.Nq * D * 2);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)a.Nk * D * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)a.Nk * D * 2);
 
@@ -296,63 +373,89 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     df[s] = __builtin_bit_cast(bf16x8, buf_load16(rd, src));
   }
   const bool q_in = qi < a.Nq;
-  const float l2q = q_in ? a.lse[((size_t)b * a.Hq + hq) * a.Nq + qi] * kLog2e : 0.0f;
-  const float ddq = q_in ? a.delta[((size_t)b * a.Hq + hq) * a.Nq + qi] : 0.0f;
+  const size_t rec = ((size_t)b * a.Hq + hq) * (size_t)a.nq_pad + qi;
+  const float l2q = q_in ? a.stats[2 * rec] : 0.0f;
+  const float ddq = q_in ? a.stats[2 * rec + 1] : 0.0f;
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
   const int swl = swz<D>(l32);
 
+  // S^T and dP^T of 32-key block kb: keys on M, this wave's queries on N
+  // (fragments read ahead of the contractions, as in the dK/dV kernel)
+  auto sdp = [&](const char* kt_l, const char* vt_l, int kb, f32x16& st, f32x16& dpt) {
+    bf16x8 ka[D / 16], va[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; s++) {
+      const int off_b = (kb * 32 + l32) * (D * 2) + (((2 * s + h32) ^ swl) << 4);
+      ka[s] = *(const bf16x8*)(kt_l + off_b);
+      va[s] = *(const bf16x8*)(vt_l + off_b);
+    }
+    st = f32x16{};
+    dpt = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; s++) {
+      st = mfma32(ka[s], qf[s], st);
+      dpt = mfma32(va[s], df[s], dpt);
+    }
+  };
+  // dS^T = P^T o (dP^T - D) into dpt; keys j0 + 32 kb + 8(r/4) + 4h + r%4
+  auto pds = [&](int j0, int kb, bool mask, const f32x16& st, f32x16& dpt) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      float p = fast_exp2(__builtin_fmaf(st[r], a.c, -l2q));
+      if (mask) {
+        const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        bool ok = q_in && (j < a.Nk);
+        if (CAUSAL) ok = ok && (j <= qi + off);
+        p = ok ? p : 0.0f;
+      }
+      dpt[r] = p * (dpt[r] - ddq);
+    }
+  };
+  // dQ^T += K^T dS^T over the 32 keys of block kb
+  auto dqk = [&](const char* kt_l, int kb, const f32x16& dpt) {
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      const int kr = kb * 32 + 16 * hf + 4 * h32 + ((lane & 15) >> 2);
+      bf16x8 ka[D / 32];
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++) {
+        const int kc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        ka[cb] = join_bf16(ds_read_tr16(kt_l + tile_off<D>(kr, kc)), ds_read_tr16(kt_l + tile_off<D>(kr + 8, kc)));
+      }
+      bf16x8 sb;
+#pragma unroll
+      for (int e = 0; e < 8; e++) sb[e] = to_bf16(dpt[8 * hf + e]);
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++) acc[cb] = mfma32(ka[cb], sb, acc[cb]);
+    }
+  };
+
   auto compute = [&](int t, const char* kt_l, const char* vt_l) {
     const int j0 = t * BN;
     if (CAUSAL && j0 > qw0 + 31 + off) return;
-    const bool need_mask = (j0 + BN > a.Nk) || !q_in || (CAUSAL && j0 + BN - 1 > qw0 + off) ||
-                           (qw0 + 32 > a.Nq);
-    f32x16 st[BN / 32], dpt[BN / 32];
+    const bool need_mask = (j0 + BN > a.Nk) || (qw0 + 32 > a.Nq) || (CAUSAL && j0 + BN - 1 > qw0 + off);
+    if (!need_mask) {
+      f32x16 st[2], dpt[2];
+      sdp(kt_l, vt_l, 0, st[0], dpt[0]);
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++) {
-      st[kb] = f32x16{};
-      dpt[kb] = f32x16{};
-    }
+      for (int kb = 0; kb < KB; kb++) {
+        if (kb + 1 < KB) sdp(kt_l, vt_l, kb + 1, st[(kb + 1) & 1], dpt[(kb + 1) & 1]);
+        pds(j0, kb, false, st[kb & 1], dpt[kb & 1]);
+        dqk(kt_l, kb, dpt[kb & 1]);
+      }
+    } else {
 #pragma unroll
-    for (int s = 0; s < D / 16; s++) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; kb++) {
-        const int off_b = (kb * 32 + l32) * (D * 2) + (((2 * s + h32) ^ swl) << 4);
-        st[kb] = mfma32(*(const bf16x8*)(kt_l + off_b), qf[s], st[kb]);
-        dpt[kb] = mfma32(*(const bf16x8*)(vt_l + off_b), df[s], dpt[kb]);
+      for (int kb = 0; kb < KB; kb++) {
+        if (CAUSAL && j0 + 32 * kb > qw0 + 31 + off) continue;
+        f32x16 st, dpt;
+        sdp(kt_l, vt_l, kb, st, dpt);
+        pds(j0, kb, true, st, dpt);
+        dqk(kt_l, kb, dpt);
       }
     }
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        float p = fast_exp2(__builtin_fmaf(st[kb][r], a.c, -l2q));
-        if (need_mask) {
-          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          bool ok = q_in && (j < a.Nk);
-          if (CAUSAL) ok = ok && (j <= qi + off);
-          if (!ok) p = 0.0f;
-        }
-        dpt[kb][r] = p * (dpt[kb][r] - ddq);
-      }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++)
-#pragma unroll
-      for (int hf = 0; hf < 2; hf++) {
-        bf16x8 sb;
-#pragma unroll
-        for (int e = 0; e < 8; e++) sb[e] = to_bf16(dpt[kb][8 * hf + e]);
-        const int kr = kb * 32 + 16 * hf + 4 * h32 + ((lane & 15) >> 2);
-#pragma unroll
-        for (int cb = 0; cb < D / 32; cb++) {
-          const int kc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-          const bf16x8 ka = join_bf16(ds_read_tr16(kt_l + tile_off<D>(kr, kc)), ds_read_tr16(kt_l + tile_off<D>(kr + 8, kc)));
-          acc[cb] = mfma32(ka, sb, acc[cb]);
-        }
-      }
   };
 
   auto step = [&](int t, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
@@ -371,7 +474,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
   }
 
   if (q_in) {
-    float* row = a.dq + q_head + (size_t)qi * D;
+    float* row = a.dq + (q_row0 + qi) * D;
 #pragma unroll
     for (int cb = 0; cb < D / 32; cb++)
 #pragma unroll
@@ -383,6 +486,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
       }
   }
 }
+
+#ifndef ATTN_BWD_BQ
+#define ATTN_BWD_BQ 64
+#endif
+#ifndef ATTN_BWD_DQ_BN
+#define ATTN_BWD_DQ_BN 64
+#endif
 
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdProblem& p, hipStream_t s) {
@@ -397,7 +507,8 @@ hipError_t launch(const BwdProblem& p, hipStream_t s) {
   a.dq = p.dq;
   a.dk = p.dk;
   a.dv = p.dv;
-  a.delta = p.delta;
+  a.stats = p.stats;
+  a.nq_pad = (int)bwd_record_rows(p.Nq);
   a.B = (int)p.B;
   a.Hq = (int)p.Hq;
   a.Hkv = (int)p.Hkv;
@@ -416,7 +527,7 @@ hipError_t launch(const BwdProblem& p, hipStream_t s) {
     BwdArgs kv = a;
     kv.n_tiles = (a.Nk + NW * 32 - 1) / (NW * 32);
     kv.n_wgs = a.B * a.Hkv * kv.n_tiles;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(kv.n_wgs), dim3(NW * 64), 0, s, kv);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, ATTN_BWD_BQ, CAUSAL>), dim3(kv.n_wgs), dim3(NW * 64), 0, s, kv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -424,7 +535,7 @@ hipError_t launch(const BwdProblem& p, hipStream_t s) {
     BwdArgs qa = a;
     qa.n_tiles = (a.Nq + NW * 32 - 1) / (NW * 32);
     qa.n_wgs = a.B * a.Hq * qa.n_tiles;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(qa.n_wgs), dim3(NW * 64), 0, s, qa);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, ATTN_BWD_DQ_BN, CAUSAL>), dim3(qa.n_wgs), dim3(NW * 64), 0, s, qa);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -25,6 +25,8 @@
 // keys) are masked elementwise.  The rescale of acc is skipped while the row
 // maximum has grown by less than kTau (log2 units): the final acc / l and
 // LSE = (m + log2 l) ln 2 are exact for any m used consistently.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -51,8 +53,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int TILE_BYTES = BN * D * 2;       // one K or V tile
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int LOADS = BN * CPR / (64 * NW);  // direct-to-LDS loads per thread per tile
+  constexpr int KB = BN / 32;                  // 32-key blocks per tile
   static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly over the workgroup");
   static_assert(BN % 32 == 0, "BN must be a multiple of 32");
+  static_assert(4 * TILE_BYTES <= 65536, "LDS offsets must fit the 16-bit immediate");
 
   // buffers: [K0 | V0 | K1 | V1]
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
@@ -114,15 +118,32 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
     qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, src));
   }
 
+  // ---- lane-constant LDS byte offsets inside a K or V tile.  The buffer, the
+  // 32-key block and the 16-row half only add multiples of 16 rows, which
+  // leave the swizzle unchanged, so they go into the instructions' immediate
+  // offsets and the tile loop does no address arithmetic.
+  const int swl = swz<D>(l32);
+  int koff[D / 16];  // A operand of S^T: key row l32, column chunk 2s + h
+#pragma unroll
+  for (int s = 0; s < D / 16; s++) koff[s] = l32 * (D * 2) + (((2 * s + h32) ^ swl) << 4);
+  int voff[D / 32][2];  // transposed V reads: rows 4h + (lane%16)/4 (+8), columns of block cb
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+    for (int lh = 0; lh < 2; lh++)
+      voff[cb][lh] = tile_off<D>(4 * h32 + ((lane & 15) >> 2) + 8 * lh, cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
   f32x16 acc[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
   float m_run = kNegInf;  // log2-domain running max used for the exponentials
   float l_run = 0.0f;     // this lane's share of the running sum
   const int qi = qw0 + l32;
-  const int swl = swz<D>(l32);
 
-  auto compute = [&](int t, const char* kt, const char* vt) {
+  auto compute = [&](int t, auto buf) {
+    constexpr int BUF = decltype(buf)::value;
+    const char* kt = smem + BUF * 2 * TILE_BYTES;
+    const char* vt = kt + TILE_BYTES;
     const int j0 = t * BN;
     // wave-level classification of the tile
     bool need_mask = (j0 + BN > a.Nk);
@@ -131,21 +152,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
       if (j0 + BN - 1 > qw0 + off) need_mask = true;  // crosses this wave's diagonal
     }
     // S^T = K Q^T
-    f32x16 st[BN / 32];
+    f32x16 st[KB];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++) st[kb] = f32x16{};
+    for (int kb = 0; kb < KB; kb++) st[kb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; s++) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; kb++) {
-        const int r = kb * 32 + l32;
-        const bf16x8 kf = *(const bf16x8*)(kt + r * (D * 2) + (((2 * s + h32) ^ swl) << 4));
+      for (int kb = 0; kb < KB; kb++) {
+        const bf16x8 kf = *(const bf16x8*)(kt + koff[s] + kb * 32 * (D * 2));
         st[kb] = mfma32(kf, qf[s], st[kb]);
       }
     }
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; kb++)
+      for (int kb = 0; kb < KB; kb++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
@@ -154,73 +174,94 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
           if (!ok) st[kb][r] = kNegInf;
         }
     }
-    // online softmax update
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[kb][r]);
-    mx = halves_max(mx) * a.c;
-    const bool grow = mx > m_run + kTau;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      // lanes that do not grow keep their state (alpha = 1; their m_run may
-      // still be -inf); a growing lane with m_run = -inf gets alpha = 0
-      const float alpha = grow ? fast_exp2(m_run - mx) : 1.0f;
-      m_run = grow ? mx : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < D / 32; cb++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[cb][r] *= alpha;
-    }
-    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+    // online softmax.  P goes to bf16 (the MFMA operand); the row sum adds the
+    // fp32 values (a sum of the bf16 values would move LSE by up to 2^-9 on
+    // short rows).  Fast path: once every row of the wave has a
+    // running max, exponentiate against it directly and accept the tile if no
+    // lane's sum exceeds 2^16 (so no P exceeds it either); only otherwise take
+    // the row max and rescale (the exact slow path below).
+    bf16x8 pb[KB][2];
     float psum = 0.0f;
+    bool fast = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
+    if (fast) {
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++)
+      for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const float p = fast_exp2(__builtin_fmaf(st[kb][r], a.c, -m_use));
-        st[kb][r] = p;
-        psum += p;
+        for (int hf = 0; hf < 2; hf++) {
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float p = fast_exp2(__builtin_fmaf(st[kb][8 * hf + e], a.c, -m_run));
+            pb[kb][hf][e] = to_bf16(p);
+            psum += p;
+          }
+        }
+      fast = __builtin_amdgcn_ballot_w64(!(psum <= 65536.0f)) == 0;
+    }
+    if (!fast) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[kb][r]);
+      mx = halves_max(mx) * a.c;
+      const bool grow = mx > m_run + kTau;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        // lanes that do not grow keep their state (alpha = 1; their m_run may
+        // still be -inf); a growing lane with m_run = -inf gets alpha = 0
+        const float alpha = grow ? fast_exp2(m_run - mx) : 1.0f;
+        m_run = grow ? mx : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) acc[cb][r] *= alpha;
       }
+      const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+      psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float p = fast_exp2(__builtin_fmaf(st[kb][8 * hf + e], a.c, -m_use));
+            pb[kb][hf][e] = to_bf16(p);
+            psum += p;
+          }
+        }
+    }
     l_run += psum;
     // O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++)
+    for (int kb = 0; kb < KB; kb++)
 #pragma unroll
       for (int hf = 0; hf < 2; hf++) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; e++) pb[e] = to_bf16(st[kb][8 * hf + e]);
-        const int kk = kb * 32 + 16 * hf;
-        const int vr = kk + 4 * h32 + ((lane & 15) >> 2);
+        const char* vk = vt + (kb * 32 + 16 * hf) * (D * 2);
 #pragma unroll
         for (int cb = 0; cb < D / 32; cb++) {
-          const int vc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-          const s16x4 lo = ds_read_tr16(vt + tile_off<D>(vr, vc));
-          const s16x4 hi = ds_read_tr16(vt + tile_off<D>(vr + 8, vc));
-          acc[cb] = mfma32(join_bf16(lo, hi), pb, acc[cb]);
+          const s16x4 lo = ds_read_tr16(vk + voff[cb][0]);
+          const s16x4 hi = ds_read_tr16(vk + voff[cb][1]);
+          acc[cb] = mfma32(join_bf16(lo, hi), pb[kb][hf], acc[cb]);
         }
       }
   };
 
   // ---- one pipeline step: prefetch tile t+1 into the other buffers, compute
-  // tile t.  The restrict-qualified buffer pointers let the compiler see that
-  // the prefetch does not write what the tile reads, so it does not wait for
-  // the prefetch before the LDS reads.
-  auto step = [&](int t, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
-                  char* __restrict__ vn) {
+  // tile t.  The prefetch writes only the other buffer pair, and each step's
+  // buffers are compile-time offsets, so the compiler can see the prefetch
+  // does not alias the tile being read.
+  using buf0 = std::integral_constant<int, 0>;
+  using buf1 = std::integral_constant<int, 1>;
+  for (int t = 0; t < n_tiles; t += 2) {
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_tiles) issue(t + 1, kn, vn);
-    compute(t, kc, vc);
-  };
-  char* const b0 = smem;
-  char* const b1 = smem + 2 * TILE_BYTES;
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, b0, b0 + TILE_BYTES, b1, b1 + TILE_BYTES);
+    if (t + 1 < n_tiles) issue(t + 1, smem + 2 * TILE_BYTES, smem + 3 * TILE_BYTES);
+    compute(t, buf0{});
     if (t + 1 >= n_tiles) break;
-    step(t + 1, b1, b1 + TILE_BYTES, b0, b0 + TILE_BYTES);
+    wait_vmem();
+    __syncthreads();
+    if (t + 2 < n_tiles) issue(t + 2, smem, smem + TILE_BYTES);
+    compute(t + 1, buf1{});
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2

@@ -49,11 +49,13 @@ struct BwdProblem {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;  // workspace: [B, Hq, Nq] fp32
+  float* stats;  // workspace: [B, Hq, bwd_record_rows(Nq)] x 2 fp32 (LSE * log2 e, D)
   int64_t B, Hq, Hkv, Nq, Nk, d;
   float scale;
   int causal;
 };
+// Rows of backward row records per head: Nq rounded up to 128.
+inline int64_t bwd_record_rows(int64_t Nq) { return (Nq + 127) / 128 * 128; }
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t s);
 
 }  // namespace attn

@@ -91,8 +91,9 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
  * Backward from the saved log-sum-exp.  Inputs q, k, v, o, dout (dtype) and
  * lse (fp32, as written by attn_fwd with the same arguments); outputs dq
  * [B,Hq,Nq,d], dk and dv [B,Hkv,Nk,d], all fp32 and fully overwritten (dk and
- * dv sum over the query heads that share a kv head).  The workspace holds the
- * per-row statistic D_i = dO_i . O_i.  Only ATTN_BF16 is built.
+ * dv sum over the query heads that share a kv head).  The workspace holds one
+ * 8-byte record per query row, (LSE * log2 e, D_i = dO_i . O_i), with the rows
+ * of each head padded to a multiple of 128.  Only ATTN_BF16 is built.
  */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d);
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
