@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn_mi355x.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["fwd_kernels.hip", "decode_kernels.hip", "bwd_kernels.hip", "attn_abi.cpp"]
+SOURCES = ["fwd_kernels.hip", "decode_kernels.hip", "bwd_kernels.hip", "bwd_dq.hip", "attn_abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -31,11 +31,11 @@ FLAGS = [
 ]
 
 
-# Per-source scheduling: the backward kernels run one wave per SIMD, so their
-# LDS operand reads must be issued well ahead of the MFMAs that use them and the
+# Per-source scheduling: the dK/dV kernel runs one wave per SIMD, so its LDS
+# operand reads must be issued well ahead of the MFMAs that use them and the
 # exponentials interleaved with independent MFMAs; the ILP-maximising machine
 # scheduler does that, the default (occupancy-driven) one sinks every read next
-# to its use.
+# to its use.  The dQ kernel (bwd_dq.hip) measured faster with the default.
 SOURCE_FLAGS = {
     "bwd_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }

@@ -1,62 +1,13 @@
-// Backward kernels for gfx950: gradients of softmax attention from the saved
-// log-sum-exp.  With s = scale * Q K^T, P = exp(s - LSE), the gradient of O
-// with respect to its inputs is
-//
-//   dV = P^T dO,   dP = dO V^T,   D_i = rowsum(dO o O)_i,   dS = P o (dP - D),
-//   dQ = scale * dS K,   dK = scale * dS^T Q,
-//
-// (the identity sum_j P_ij dP_ij = dO_i . O_i gives D without a pass over
-// keys).  "Não escreva kernels, derive-os" (FAQ entry "O que o Tang propõe de
-// diferente?") obtains its backward by rewriting and notes in "Aprofundamento"
-// (third paragraph) that a fused bf16 backward missed an fp32 tolerance; this
-// build keeps bf16 MFMA operands with fp32 accumulation and writes fp32
-// gradients.
-//
-// Three kernels, no atomics (every output element has one writer):
-//   bwd_pre   per query row: (LSE * log2 e, D_i = dO_i . O_i) into the
-//             workspace, one 8-byte record per row
-//   bwd_dkdv  workgroup = (b, kv head, 32*NW keys).  K and V fragments stay in
-//             registers; for every query head of the group and every query
-//             tile that can see the keys, Q, dO and the row records stream
-//             through LDS (double-buffered, direct-to-LDS loads).
-//             S = Q K^T and dP = dO V^T put keys on the MFMA N dimension, so
-//             P and dS come out with one key per lane and feed
-//             dV += P^T dO and dK += dS^T Q straight from registers, with dO
-//             and Q read transposed from LDS.
-//   bwd_dq    workgroup = (b, query head, 32*NW queries), the forward's
-//             layout: S^T = K Q^T and dP^T = V dO^T keep one query per lane;
-//             dQ^T += K^T dS^T reads K transposed from LDS.
-//
-// Both main kernels run one wave per SIMD (their live fragments and
-// accumulators exceed half the register file), so the softmax-gradient VALU
-// work is overlapped with MFMA work inside each wave: the loop over 32-row
-// (or 32-key) blocks is software-pipelined so that the contractions of block
-// i+1 are independent of, and issued around, the exponentials of block i.
-#include "device_common.hpp"
-#include "kernels.h"
+// Backward kernels of softmax attention on gfx950, part 1: the per-row
+// records and dK, dV (the formulas and the kernel split are stated in
+// bwd_common.hpp).
+#include "bwd_common.hpp"
 
 namespace attn {
 
 namespace {
 
-struct BwdArgs {
-  const __bf16* q;
-  const __bf16* k;
-  const __bf16* v;
-  const __bf16* o;
-  const __bf16* dout;
-  const float* lse;
-  float* dq;
-  float* dk;
-  float* dv;
-  float* stats;  // [B, Hq, nq_pad] x (LSE * log2 e, D)
-  int B, Hq, Hkv, Nq, Nk, g;
-  int nq_pad;    // record rows per head: Nq rounded up to 128, so that the
-                 // 16-byte loads of records never straddle the end of a head
-  int n_tiles, n_wgs;
-  float c;      // scale * log2(e)
-  float scale;
-};
+using bwd::BwdArgs;
 
 // Row record: (LSE in log2 units, D_i).  A row with no visible key has
 // LSE = -inf; its record holds +inf so that every P of the row is 0.
@@ -89,15 +40,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // dK, dV.  Each wave owns 32 keys; a query tile of BQ rows is processed in
 // 32-row blocks.
 template <int D, int NW, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, ATTN_BWD_KV_OCC) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int TILE = BQ * D * 2;  // bytes of one Q or dO tile
   constexpr int STAGE = 2 * TILE + 1024;  // Q, dO, row records (BQ * 8 <= 1024 bytes)
+  constexpr int NS = ATTN_BWD_STAGES;     // query tiles in flight
+  static_assert(NS == 2 || NS == 3, "two or three stages");
   constexpr int CPR = D / 8;
   constexpr int LOADS = BQ * CPR / (64 * NW);
+  constexpr int VM_PER_TILE = 2 * LOADS + 1;  // vector-memory loads per wave per tile
   constexpr int NB = BQ / 32;  // 32-row blocks per tile
   static_assert(LOADS * 64 * NW == BQ * CPR, "tile must split evenly");
   static_assert(BQ % 32 == 0 && BQ * 8 <= 1024, "BQ must be 32, 64, 96 or 128");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];  // [Q0 | dO0 | R0 | Q1 | dO1 | R1]
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];  // per stage: [Q | dO | records]
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -161,9 +115,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
       buf_load_lds16(rq, src, (lds_void*)(st_l + slab * 1024));
       buf_load_lds16(rd, src, (lds_void*)(st_l + TILE + slab * 1024));
     }
-    if (wave == NW - 1) {
+    {
       // row records of rows i0 .. i0 + 127 (the first BQ are used); rows past
-      // nq_pad read as zeros, rows past Nq are masked
+      // nq_pad read as zeros, rows past Nq are masked.  Every wave loads the
+      // same 1 KB (identical bytes), so every wave issues the same number of
+      // loads per tile and can wait for an older tile by count.
       const size_t rec0 = ((size_t)b * a.Hq + hq) * (size_t)a.nq_pad;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.stats + 2 * rec0, (uint32_t)a.nq_pad * 8);
       buf_load_lds16(rs, (uint32_t)(i0 * 8 + lane * 16), (lds_void*)(st_l + 2 * TILE));
@@ -255,7 +211,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int i0 = qtile_of(it) * BQ;
     if (CAUSAL && i0 + BQ - 1 + off < jw) return;  // no query of the tile sees this wave's keys
     const bool need_mask = (i0 + BQ > a.Nq) || (jw + 32 > a.Nk) || (CAUSAL && i0 + off < jw + 31);
-    if (!need_mask) {
+    if (!need_mask && !ATTN_BWD_PIPE) {
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) {
+        f32x16 sa, da;
+        sdp(st_l, nb, sa, da);
+        pds(st_l, nb, i0, false, sa, da);
+        dvdk(st_l, nb, sa, da);
+      }
+    } else if (!need_mask) {
       // software pipeline over the 32-row blocks: the S/dP contractions of
       // block nb + 1 are issued before the P/dS arithmetic of block nb
       f32x16 sa[2], da[2];
@@ -278,19 +242,38 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
+  // One step: wait until tile it has landed (with NS = 3, tile it + 1 may
+  // still be in flight), barrier, prefetch tile it + NS - 1 into the stage
+  // that tile it - 1 used, compute tile it.  Restrict: the prefetch never
+  // writes the stage being read.
   auto step = [&](int it, const char* __restrict__ cur, char* __restrict__ nxt) {
-    wait_vmem();
-    __syncthreads();
-    if (it + 1 < n_iter) issue(it + 1, nxt);
+    if (NS == 3 && it + 1 < n_iter)
+      wait_vmem_n<VM_PER_TILE>();
+    else
+      wait_vmem();
+    barrier_nofence();
+    if (it + NS - 1 < n_iter) issue(it + NS - 1, nxt);
     compute(it, cur);
   };
   char* const s0 = smem;
   char* const s1 = smem + STAGE;
+  char* const s2 = smem + (NS - 1) * STAGE;  // = s1 when NS == 2
   if (n_iter > 0) issue(0, s0);
-  for (int it = 0; it < n_iter; it += 2) {
-    step(it, s0, s1);
-    if (it + 1 >= n_iter) break;
-    step(it + 1, s1, s0);
+  if (NS == 3 && n_iter > 1) issue(1, s1);
+  if (NS == 3) {
+    for (int it = 0; it < n_iter; it += 3) {
+      step(it, s0, s2);
+      if (it + 1 >= n_iter) break;
+      step(it + 1, s1, s0);
+      if (it + 2 >= n_iter) break;
+      step(it + 2, s2, s1);
+    }
+  } else {
+    for (int it = 0; it < n_iter; it += 2) {
+      step(it, s0, s1);
+      if (it + 1 >= n_iter) break;
+      step(it + 1, s1, s0);
+    }
   }
 
   // dV, dK accumulators: lane holds dim cb*32 + l32 of keys jw + 8(r/4) + 4h + r%4
@@ -308,191 +291,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 }
-
-// ---------------------------------------------------------------------------
-// dQ.  Each wave owns 32 query rows; key tiles of BN keys stream through LDS
-// and are processed in 32-key blocks.
-template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int TILE = BN * D * 2;
-  constexpr int CPR = D / 8;
-  constexpr int LOADS = BN * CPR / (64 * NW);
-  constexpr int KB = BN / 32;
-  static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly");
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // [K0 | V0 | K1 | V1]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int h32 = lane >> 5;
-  const int l32 = lane & 31;
-
-  const int work = xcd_remap(blockIdx.x, a.n_wgs);
-  const int per_pair = a.g * a.n_tiles;
-  const int pair = work / per_pair;
-  const int rem = work % per_pair;
-  const int qt = CAUSAL ? (a.n_tiles - 1 - rem / a.g) : (rem / a.g);
-  const int hq = (pair % a.Hkv) * a.g + rem % a.g;
-  const int b = pair / a.Hkv;
-  const int kvh = pair % a.Hkv;
-  const int i0 = qt * NW * 32;
-  const int qw0 = i0 + wave * 32;
-  const int qi = qw0 + l32;
-  const int off = a.Nk - a.Nq;
-
-  const size_t q_row0 = ((size_t)b * a.Hq + hq) * (size_t)a.Nq;
-  const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_row0 * D, (uint32_t)a.Nq * D * 2);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + q_row0 * D, (uint32_t)a.Nq * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)a.Nk * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)a.Nk * D * 2);
-
-  int kend = a.Nk;
-  if (CAUSAL) kend = min(a.Nk, min(i0 + NW * 32, a.Nq) - 1 + off + 1);
-  const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
-
-  auto issue = [&](int t, char* kt_l, char* vt_l) {
-    const int j0 = t * BN;
-#pragma unroll
-    for (int n = 0; n < LOADS; n++) {
-      const int slab = n * NW + wave;
-      const int p = slab * 64 + lane;
-      const int r = p / CPR;
-      const int cc = (p % CPR) ^ swz<D>(r);
-      const uint32_t src = (uint32_t)(((j0 + r) * D + cc * 8) * 2);
-      buf_load_lds16(rk, src, (lds_void*)(kt_l + slab * 1024));
-      buf_load_lds16(rv, src, (lds_void*)(vt_l + slab * 1024));
-    }
-  };
-  if (n_kt > 0) issue(0, smem, smem + TILE);
-
-  bf16x8 qf[D / 16], df[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; s++) {
-    const uint32_t src = (uint32_t)((qi * D + 16 * s + 8 * h32) * 2);
-    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, src));
-    df[s] = __builtin_bit_cast(bf16x8, buf_load16(rd, src));
-  }
-  const bool q_in = qi < a.Nq;
-  const size_t rec = ((size_t)b * a.Hq + hq) * (size_t)a.nq_pad + qi;
-  const float l2q = q_in ? a.stats[2 * rec] : 0.0f;
-  const float ddq = q_in ? a.stats[2 * rec + 1] : 0.0f;
-
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
-  const int swl = swz<D>(l32);
-
-  // S^T and dP^T of 32-key block kb: keys on M, this wave's queries on N
-  // (fragments read ahead of the contractions, as in the dK/dV kernel)
-  auto sdp = [&](const char* kt_l, const char* vt_l, int kb, f32x16& st, f32x16& dpt) {
-    bf16x8 ka[D / 16], va[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; s++) {
-      const int off_b = (kb * 32 + l32) * (D * 2) + (((2 * s + h32) ^ swl) << 4);
-      ka[s] = *(const bf16x8*)(kt_l + off_b);
-      va[s] = *(const bf16x8*)(vt_l + off_b);
-    }
-    st = f32x16{};
-    dpt = f32x16{};
-#pragma unroll
-    for (int s = 0; s < D / 16; s++) {
-      st = mfma32(ka[s], qf[s], st);
-      dpt = mfma32(va[s], df[s], dpt);
-    }
-  };
-  // dS^T = P^T o (dP^T - D) into dpt; keys j0 + 32 kb + 8(r/4) + 4h + r%4
-  auto pds = [&](int j0, int kb, bool mask, const f32x16& st, f32x16& dpt) {
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      float p = fast_exp2(__builtin_fmaf(st[r], a.c, -l2q));
-      if (mask) {
-        const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-        bool ok = q_in && (j < a.Nk);
-        if (CAUSAL) ok = ok && (j <= qi + off);
-        p = ok ? p : 0.0f;
-      }
-      dpt[r] = p * (dpt[r] - ddq);
-    }
-  };
-  // dQ^T += K^T dS^T over the 32 keys of block kb
-  auto dqk = [&](const char* kt_l, int kb, const f32x16& dpt) {
-#pragma unroll
-    for (int hf = 0; hf < 2; hf++) {
-      const int kr = kb * 32 + 16 * hf + 4 * h32 + ((lane & 15) >> 2);
-      bf16x8 ka[D / 32];
-#pragma unroll
-      for (int cb = 0; cb < D / 32; cb++) {
-        const int kc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        ka[cb] = join_bf16(ds_read_tr16(kt_l + tile_off<D>(kr, kc)), ds_read_tr16(kt_l + tile_off<D>(kr + 8, kc)));
-      }
-      bf16x8 sb;
-#pragma unroll
-      for (int e = 0; e < 8; e++) sb[e] = to_bf16(dpt[8 * hf + e]);
-#pragma unroll
-      for (int cb = 0; cb < D / 32; cb++) acc[cb] = mfma32(ka[cb], sb, acc[cb]);
-    }
-  };
-
-  auto compute = [&](int t, const char* kt_l, const char* vt_l) {
-    const int j0 = t * BN;
-    if (CAUSAL && j0 > qw0 + 31 + off) return;
-    const bool need_mask = (j0 + BN > a.Nk) || (qw0 + 32 > a.Nq) || (CAUSAL && j0 + BN - 1 > qw0 + off);
-    if (!need_mask) {
-      f32x16 st[2], dpt[2];
-      sdp(kt_l, vt_l, 0, st[0], dpt[0]);
-#pragma unroll
-      for (int kb = 0; kb < KB; kb++) {
-        if (kb + 1 < KB) sdp(kt_l, vt_l, kb + 1, st[(kb + 1) & 1], dpt[(kb + 1) & 1]);
-        pds(j0, kb, false, st[kb & 1], dpt[kb & 1]);
-        dqk(kt_l, kb, dpt[kb & 1]);
-      }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KB; kb++) {
-        if (CAUSAL && j0 + 32 * kb > qw0 + 31 + off) continue;
-        f32x16 st, dpt;
-        sdp(kt_l, vt_l, kb, st, dpt);
-        pds(j0, kb, true, st, dpt);
-        dqk(kt_l, kb, dpt);
-      }
-    }
-  };
-
-  auto step = [&](int t, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
-                  char* __restrict__ vn) {
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < n_kt) issue(t + 1, kn, vn);
-    compute(t, kc, vc);
-  };
-  char* const b0 = smem;
-  char* const b1 = smem + 2 * TILE;
-  for (int t = 0; t < n_kt; t += 2) {
-    step(t, b0, b0 + TILE, b1, b1 + TILE);
-    if (t + 1 >= n_kt) break;
-    step(t + 1, b1, b1 + TILE, b0, b0 + TILE);
-  }
-
-  if (q_in) {
-    float* row = a.dq + (q_row0 + qi) * D;
-#pragma unroll
-    for (int cb = 0; cb < D / 32; cb++)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; g4++) {
-        f32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; e++) w[e] = acc[cb][4 * g4 + e] * a.scale;
-        *(f32x4*)(row + cb * 32 + 8 * g4 + 4 * h32) = w;
-      }
-  }
-}
-
-#ifndef ATTN_BWD_BQ
-#define ATTN_BWD_BQ 64
-#endif
-#ifndef ATTN_BWD_DQ_BN
-#define ATTN_BWD_DQ_BN 64
-#endif
 
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdProblem& p, hipStream_t s) {
@@ -531,13 +329,7 @@ hipError_t launch(const BwdProblem& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (rows > 0) {
-    BwdArgs qa = a;
-    qa.n_tiles = (a.Nq + NW * 32 - 1) / (NW * 32);
-    qa.n_wgs = a.B * a.Hq * qa.n_tiles;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, ATTN_BWD_DQ_BN, CAUSAL>), dim3(qa.n_wgs), dim3(NW * 64), 0, s, qa);
-    return hipGetLastError();
-  }
+  if (rows > 0) return bwd::launch_dq(a, D, CAUSAL, s);
   return hipSuccess;
 }
 

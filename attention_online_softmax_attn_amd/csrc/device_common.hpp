@@ -55,6 +55,25 @@ __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_
 // Wait until this wave's outstanding vector-memory loads (including direct-to-LDS
 // loads) have completed; expcnt and lgkmcnt are left unconstrained.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier without the release/acquire fences of __syncthreads()
+// (the release fence waits for every outstanding load, including prefetches
+// of later tiles).  The caller must already have waited (wait_vmem /
+// wait_vmem_n) for the direct-to-LDS loads whose data the barrier publishes.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (loads complete in issue order for this count); N < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -48,17 +48,20 @@ struct FwdArgs {
 };
 
 template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int TILE_BYTES = BN * D * 2;       // one K or V tile
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int LOADS = BN * CPR / (64 * NW);  // direct-to-LDS loads per thread per tile
-  constexpr int KB = BN / 32;                  // 32-key blocks per tile
+  constexpr int KS = 64;                       // keys per sub-tile (the unit of S, softmax and PV)
+  constexpr int KB = KS / 32;                  // 32-key blocks per sub-tile
   static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly over the workgroup");
-  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
-  static_assert(4 * TILE_BYTES <= 65536, "LDS offsets must fit the 16-bit immediate");
+  static_assert(BN % KS == 0, "BN must be a multiple of 64");
+  static_assert(2 * TILE_BYTES <= 65536, "LDS offsets must fit the 16-bit immediate");
 
-  // buffers: [K0 | V0 | K1 | V1]
+  // buffers: [K0 | K1 | V0 | V1]; reads address K through koff and V through
+  // voff (which include the V0 base), the buffer, sub-tile, key block and row
+  // half through the immediate offset (at most 2 * TILE_BYTES - 16 rows)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  if (n_tiles > 0) issue(0, smem, smem + TILE_BYTES);
+  if (n_tiles > 0) issue(0, smem, smem + 2 * TILE_BYTES);
 
   // ---- Q fragments (B operand of S^T = K Q^T): row qw0 + l32, dims 16s + 8h .. +8
   bf16x8 qf[D / 16];
@@ -131,7 +134,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int cb = 0; cb < D / 32; cb++)
 #pragma unroll
     for (int lh = 0; lh < 2; lh++)
-      voff[cb][lh] = tile_off<D>(4 * h32 + ((lane & 15) >> 2) + 8 * lh, cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+      voff[cb][lh] = 2 * TILE_BYTES +
+                     tile_off<D>(4 * h32 + ((lane & 15) >> 2) + 8 * lh, cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -140,16 +144,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   float l_run = 0.0f;     // this lane's share of the running sum
   const int qi = qw0 + l32;
 
-  auto compute = [&](int t, auto buf) {
+  // one 64-key sub-tile at key offset 64 * SUB of the tile in buffer BUF
+  auto compute_sub = [&](int t, auto buf, auto sub) {
     constexpr int BUF = decltype(buf)::value;
-    const char* kt = smem + BUF * 2 * TILE_BYTES;
-    const char* vt = kt + TILE_BYTES;
-    const int j0 = t * BN;
-    // wave-level classification of the tile
-    bool need_mask = (j0 + BN > a.Nk);
+    constexpr int SUB = decltype(sub)::value;
+    const char* kt = smem + BUF * TILE_BYTES + SUB * KS * (D * 2);
+    const char* vt = smem + BUF * TILE_BYTES + SUB * KS * (D * 2);  // + voff, which holds the V0 base
+    const int j0 = t * BN + SUB * KS;
+    // wave-level classification of the sub-tile
+    if (j0 >= a.Nk) return;
+    bool need_mask = (j0 + KS > a.Nk);
     if (CAUSAL) {
       if (j0 > qw0 + 31 + off) return;               // nothing visible to this wave
-      if (j0 + BN - 1 > qw0 + off) need_mask = true;  // crosses this wave's diagonal
+      if (j0 + KS - 1 > qw0 + off) need_mask = true;  // crosses this wave's diagonal
     }
     // S^T = K Q^T
     f32x16 st[KB];
@@ -246,6 +253,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
       }
   };
 
+  auto compute = [&](int t, auto buf) {
+    compute_sub(t, buf, std::integral_constant<int, 0>{});
+    if constexpr (BN / KS > 1) compute_sub(t, buf, std::integral_constant<int, 1>{});
+    static_assert(BN / KS <= 2, "at most two sub-tiles");
+  };
+
   // ---- one pipeline step: prefetch tile t+1 into the other buffers, compute
   // tile t.  The prefetch writes only the other buffer pair, and each step's
   // buffers are compile-time offsets, so the compiler can see the prefetch
@@ -255,12 +268,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int t = 0; t < n_tiles; t += 2) {
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_tiles) issue(t + 1, smem + 2 * TILE_BYTES, smem + 3 * TILE_BYTES);
+    if (t + 1 < n_tiles) issue(t + 1, smem + TILE_BYTES, smem + 3 * TILE_BYTES);
     compute(t, buf0{});
     if (t + 1 >= n_tiles) break;
     wait_vmem();
     __syncthreads();
-    if (t + 2 < n_tiles) issue(t + 2, smem, smem + TILE_BYTES);
+    if (t + 2 < n_tiles) issue(t + 2, smem, smem + 2 * TILE_BYTES);
     compute(t + 1, buf1{});
   }
 
@@ -444,10 +457,28 @@ hipError_t launch_f32(const FwdProblem& p, hipStream_t s) {
 
 }  // namespace
 
+#ifndef ATTN_FWD_BIG_NW
+#define ATTN_FWD_BIG_NW 8
+#endif
+#ifndef ATTN_FWD_BIG_BN
+#define ATTN_FWD_BIG_BN 64
+#endif
+
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
   const bool causal = p.causal != 0;
   if (p.bf16) {
-    if (p.d == 128) return causal ? launch_bf16<128, 4, 64, true>(p, s) : launch_bf16<128, 4, 64, false>(p, s);
+    // Large problems: 8 waves (256 query rows) per workgroup, which share
+    // each K/V tile (half the tile loads and barriers per query row of the
+    // small configuration); measured faster once there are at least 8 such
+    // workgroups per CU (N = 16384 and 44032 at 32 heads), slower at 2 per CU
+    // (4 x 16 heads x 2048).  Small problems: 4 waves, two workgroups per CU.
+    constexpr int NWB = ATTN_FWD_BIG_NW, BNB = ATTN_FWD_BIG_BN;
+    const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= 8 * 256;
+    if (p.d == 128) {
+      if (big) return causal ? launch_bf16<128, NWB, BNB, true>(p, s) : launch_bf16<128, NWB, BNB, false>(p, s);
+      return causal ? launch_bf16<128, 4, 64, true>(p, s) : launch_bf16<128, 4, 64, false>(p, s);
+    }
+    if (big) return causal ? launch_bf16<64, NWB, BNB, true>(p, s) : launch_bf16<64, NWB, BNB, false>(p, s);
     return causal ? launch_bf16<64, 4, 64, true>(p, s) : launch_bf16<64, 4, 64, false>(p, s);
   }
   if (p.d == 128) return causal ? launch_f32<128, true>(p, s) : launch_f32<128, false>(p, s);
