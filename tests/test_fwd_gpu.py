@@ -141,6 +141,51 @@ def test_no_writes_outside_outputs():
     assert guards_intact(ofull, o.numel()) and guards_intact(lfull, lse.numel())
 
 
+# ---------------------------------------------------------------- large grids (the 8-wave ping-pong kernel)
+# Problems with at least 8 workgroups of 256 query rows per CU (>= 2048 of
+# them) run the 8-wave kernel; these shapes reach it with ragged lengths,
+# grouped-query heads and Nq != Nk, checked on sampled rows (the oracle of a
+# whole 8k x 8k problem would take minutes on the host).
+LARGE = [
+    # B, Hq, Hkv, Nq, Nk, d
+    (2, 32, 8, 8200, 8200, 128),
+    (2, 32, 8, 8100, 8300, 128),    # Nq < Nk
+    (1, 64, 8, 8300, 8100, 64),     # Nq > Nk: causal rows with no visible key
+]
+
+
+@pytest.mark.parametrize("shape", LARGE)
+@pytest.mark.parametrize("causal", [True, False])
+def test_large_grid_sampled_rows(oracle_mod, shape, causal):
+    B, Hq, Hkv, Nq, Nk, d = shape
+    assert B * Hq * ((Nq + 255) // 256) >= 8 * 256
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = synth.attn_inputs(600 + Nq + d, B, Hq, Hkv, Nq, Nk, d, bf16=True)
+    print(f"large case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal}", flush=True)
+    o, lse = attn_fwd(dev(q, True), dev(k, True), dev(v, True), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    forced = (0, 1, 63, 64, 255, 256, 257, Nq // 2, Nq - 65, Nq - 2, Nq - 1)
+    rows = synth.sample_rows(40005 + Nq, 192, B, Hq, Nq, forced_i=forced)
+    eo, el = oracle_mod.fwd_rows(q, k, v, rows, scale, causal)
+    idx = (rows[:, 0], rows[:, 1], rows[:, 2])
+    assert_close("O sampled", host(o[idx[0], idx[1], idx[2]]), eo, TOL_O_BF16)
+    assert_close("LSE sampled", host(lse[idx[0], idx[1], idx[2]]), el, TOL_LSE_BF16)
+
+
+def test_large_grid_peaked(oracle_mod):
+    # sharpened scores through the 8-wave kernel's exact (max / rescale) path
+    B, Hq, Hkv, N, d = 2, 32, 8, 8200, 128
+    q, k, v = synth.attn_inputs(650, B, Hq, Hkv, N, N, d, bf16=True, qk_scale=4.0)
+    o, lse = attn_fwd(dev(q, True), dev(k, True), dev(v, True), causal=True)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(40650, 128, B, Hq, N, forced_i=(0, 1, 255, 256, N - 1))
+    eo, el = oracle_mod.fwd_rows(q, k, v, rows, 1.0 / math.sqrt(d), True)
+    idx = (rows[:, 0], rows[:, 1], rows[:, 2])
+    tol = 2.0 ** -8 * (float(np.abs(v).max()) + float(np.abs(eo).max())) + 1e-3
+    assert_close("O sampled", host(o[idx[0], idx[1], idx[2]]), eo, tol)
+    assert_close("LSE sampled", host(lse[idx[0], idx[1], idx[2]]), el, TOL_LSE_BF16)
+
+
 # ---------------------------------------------------------------- full size, long causal prefill
 # B=1, Hq=32, Hkv=8, d=128, N=44032, bf16 ~ N(0,1)
 
