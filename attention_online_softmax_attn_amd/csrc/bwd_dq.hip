@@ -21,7 +21,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_Q_OCC) void bwd_dq_kernel(BwdArgs
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // [K0 | V0 | K1 | V1]
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_KV_OCC) void bwd_dkdv_kernel(BwdA
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];  // per stage: [Q | dO | records]
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 

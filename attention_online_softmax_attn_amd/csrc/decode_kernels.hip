@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   __shared__ __attribute__((aligned(1024))) char smem[kWaves * 2 * STAGE];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 

@@ -109,6 +109,10 @@ __device__ __forceinline__ float halves_sum(float x) { return x + partner32(x); 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value, so
+// that index arithmetic and branches derived from it stay on the scalar unit.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 
 // fp32 -> bf16, round to nearest even (inputs here are finite or +-0).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }

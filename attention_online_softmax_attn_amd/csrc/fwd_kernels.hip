@@ -65,7 +65,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
