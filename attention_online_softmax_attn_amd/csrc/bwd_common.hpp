@@ -28,11 +28,12 @@
 //             layout: S^T = K Q^T and dP^T = V dO^T keep one query per lane;
 //             dQ^T += K^T dS^T reads K transposed from LDS.
 //
-// Both main kernels run one wave per SIMD (their live fragments and
-// accumulators exceed half the register file), so the softmax-gradient VALU
+// The dK/dV kernel runs one wave per SIMD (its K, V fragments and dK, dV
+// accumulators exceed half the register file), so its softmax-gradient VALU
 // work is overlapped with MFMA work inside each wave: the loop over 32-row
-// (or 32-key) blocks is software-pipelined so that the contractions of block
-// i+1 are independent of, and issued around, the exponentials of block i.
+// blocks is software-pipelined so that the contractions of block i+1 are
+// independent of, and issued around, the exponentials of block i.  The dQ
+// kernel fits two waves per SIMD, which overlap each other.
 #pragma once
 
 #include "device_common.hpp"
@@ -43,19 +44,13 @@
 #ifndef ATTN_BWD_KV_OCC
 #define ATTN_BWD_KV_OCC 1
 #endif
-#ifndef ATTN_BWD_Q_OCC
-#define ATTN_BWD_Q_OCC 1
-#endif
-// 1: software-pipeline the 32-row / 32-key blocks of unmasked tiles
+// 1: software-pipeline the 32-row blocks of unmasked tiles (dK/dV kernel)
 #ifndef ATTN_BWD_PIPE
 #define ATTN_BWD_PIPE 1
 #endif
 
 #ifndef ATTN_BWD_BQ
 #define ATTN_BWD_BQ 64
-#endif
-#ifndef ATTN_BWD_DQ_BN
-#define ATTN_BWD_DQ_BN 128
 #endif
 
 // Pipeline depth of the dK/dV kernel: query tiles in flight (the tile being

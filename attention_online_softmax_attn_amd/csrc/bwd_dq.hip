@@ -1,6 +1,8 @@
 // Backward kernels of softmax attention on gfx950, part 2: dQ (the formulas
 // and the kernel split are stated in bwd_common.hpp).  Built with the default
 // machine scheduler; the dK/dV file uses the ILP-maximising one.
+#include <type_traits>
+
 #include "bwd_common.hpp"
 
 namespace attn {
@@ -9,16 +11,23 @@ namespace bwd {
 namespace {
 
 // ---------------------------------------------------------------------------
-// dQ.  Each wave owns 32 query rows; key tiles of BN keys stream through LDS
-// and are processed in 32-key blocks.
-template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, ATTN_BWD_Q_OCC) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int TILE = BN * D * 2;
+// dQ, two waves per SIMD.  The forward kernel's organisation: NW waves of 32
+// query rows each share 64-key K/V tiles double-buffered in LDS (direct-to-LDS
+// loads, buffers at compile-time offsets, lane-constant LDS offsets with the
+// buffer, key block and row half in the immediate), and each wave works one
+// 32-key block at a time so that fragments, accumulators and the block's
+// S^T / dP^T fit the 256 registers a wave has when two share a SIMD; the SIMD
+// then overlaps one wave's exponentials with the other's MFMAs.
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BN = 64;
+  constexpr int TILE = BN * D * 2;            // one K or V tile
   constexpr int CPR = D / 8;
-  constexpr int LOADS = BN * CPR / (64 * NW);
+  constexpr int LOADS = BN * CPR / (64 * NW);  // direct-to-LDS loads per thread per K (or V) tile
   constexpr int KB = BN / 32;
   static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly");
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // [K0 | V0 | K1 | V1]
+  static_assert(4 * TILE <= 65536, "LDS offsets must fit the 16-bit immediate");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // [K0 | K1 | V0 | V1]
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -62,7 +71,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_Q_OCC) void bwd_dq_kernel(BwdArgs
       buf_load_lds16(rv, src, (lds_void*)(vt_l + slab * 1024));
     }
   };
-  if (n_kt > 0) issue(0, smem, smem + TILE);
+  if (n_kt > 0) issue(0, smem, smem + 2 * TILE);
 
   bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
@@ -76,117 +85,88 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_Q_OCC) void bwd_dq_kernel(BwdArgs
   const float l2q = q_in ? a.stats[2 * rec] : 0.0f;
   const float ddq = q_in ? a.stats[2 * rec + 1] : 0.0f;
 
+  // lane-constant LDS offsets: rows l32, chunk 2s + h of a K (or V) tile for
+  // the A operands of S^T and dP^T; transposed K reads for the A operand of
+  // dQ^T (rows 4h + (lane%16)/4 (+8), columns of block cb)
+  const int swl = swz<D>(l32);
+  int aoff[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; s++) aoff[s] = l32 * (D * 2) + (((2 * s + h32) ^ swl) << 4);
+  int toff[D / 32][2];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+    for (int lh = 0; lh < 2; lh++)
+      toff[cb][lh] = tile_off<D>(4 * h32 + ((lane & 15) >> 2) + 8 * lh, cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
   f32x16 acc[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
-  const int swl = swz<D>(l32);
 
-  // S^T and dP^T of 32-key block kb: keys on M, this wave's queries on N
-  // (fragments read ahead of the contractions, as in the dK/dV kernel)
-  auto sdp = [&](const char* kt_l, const char* vt_l, int kb, f32x16& st, f32x16& dpt) {
-    st = f32x16{};
-    dpt = f32x16{};
-    if (ATTN_BWD_PIPE) {
-      bf16x8 ka[D / 16], va[D / 16];
+  // one 32-key block kb of tile t in buffer BUF
+  auto block = [&](int t, auto buf, auto kbc) {
+    constexpr int BUF = decltype(buf)::value;
+    constexpr int kb = decltype(kbc)::value;
+    const int j0 = t * BN + kb * 32;
+    if (CAUSAL && j0 > qw0 + 31 + off) return;  // no key of the block visible to this wave
+    const bool need_mask = (j0 + 32 > a.Nk) || (qw0 + 32 > a.Nq) || (CAUSAL && j0 + 31 > qw0 + off);
+    const char* kt = smem + BUF * TILE + kb * 32 * (D * 2);
+    const char* vt = smem + (2 + BUF) * TILE + kb * 32 * (D * 2);
+    // S^T = K Q^T and dP^T = V dO^T: keys on M, this wave's queries on N
+    f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
-      for (int s = 0; s < D / 16; s++) {
-        const int off_b = (kb * 32 + l32) * (D * 2) + (((2 * s + h32) ^ swl) << 4);
-        ka[s] = *(const bf16x8*)(kt_l + off_b);
-        va[s] = *(const bf16x8*)(vt_l + off_b);
-      }
-#pragma unroll
-      for (int s = 0; s < D / 16; s++) {
-        st = mfma32(ka[s], qf[s], st);
-        dpt = mfma32(va[s], df[s], dpt);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < D / 16; s++) {
-        const int off_b = (kb * 32 + l32) * (D * 2) + (((2 * s + h32) ^ swl) << 4);
-        st = mfma32(*(const bf16x8*)(kt_l + off_b), qf[s], st);
-        dpt = mfma32(*(const bf16x8*)(vt_l + off_b), df[s], dpt);
-      }
+    for (int s = 0; s < D / 16; s++) {
+      st = mfma32(*(const bf16x8*)(kt + aoff[s]), qf[s], st);
+      dpt = mfma32(*(const bf16x8*)(vt + aoff[s]), df[s], dpt);
     }
-  };
-  // dS^T = P^T o (dP^T - D) into dpt; keys j0 + 32 kb + 8(r/4) + 4h + r%4
-  auto pds = [&](int j0, int kb, bool mask, const f32x16& st, f32x16& dpt) {
+    // dS^T = P^T o (dP^T - D); keys j0 + 8(r/4) + 4h + r%4
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-      float p = fast_exp2(__builtin_fmaf(st[r], a.c, -l2q));
-      if (mask) {
-        const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      const float p = fast_exp2(__builtin_fmaf(st[r], a.c, -l2q));
+      float ds = p * (dpt[r] - ddq);
+      if (need_mask) {
+        const int j = j0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
         bool ok = q_in && (j < a.Nk);
         if (CAUSAL) ok = ok && (j <= qi + off);
-        p = ok ? p : 0.0f;
+        ds = ok ? ds : 0.0f;
       }
-      dpt[r] = p * (dpt[r] - ddq);
+      dpt[r] = ds;
     }
-  };
-  // dQ^T += K^T dS^T over the 32 keys of block kb
-  auto dqk = [&](const char* kt_l, int kb, const f32x16& dpt) {
+    // dQ^T += K^T dS^T, 16 keys per MFMA (K read transposed)
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-      const int kr = kb * 32 + 16 * hf + 4 * h32 + ((lane & 15) >> 2);
-      bf16x8 ka[D / 32];
-#pragma unroll
-      for (int cb = 0; cb < D / 32; cb++) {
-        const int kc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        ka[cb] = join_bf16(ds_read_tr16(kt_l + tile_off<D>(kr, kc)), ds_read_tr16(kt_l + tile_off<D>(kr + 8, kc)));
-      }
       bf16x8 sb;
 #pragma unroll
       for (int e = 0; e < 8; e++) sb[e] = to_bf16(dpt[8 * hf + e]);
+      const char* kk = kt + 16 * hf * (D * 2);
 #pragma unroll
-      for (int cb = 0; cb < D / 32; cb++) acc[cb] = mfma32(ka[cb], sb, acc[cb]);
-    }
-  };
-
-  auto compute = [&](int t, const char* kt_l, const char* vt_l) {
-    const int j0 = t * BN;
-    if (CAUSAL && j0 > qw0 + 31 + off) return;
-    const bool need_mask = (j0 + BN > a.Nk) || (qw0 + 32 > a.Nq) || (CAUSAL && j0 + BN - 1 > qw0 + off);
-    if (!need_mask && !ATTN_BWD_PIPE) {
-#pragma unroll
-      for (int kb = 0; kb < KB; kb++) {
-        f32x16 st, dpt;
-        sdp(kt_l, vt_l, kb, st, dpt);
-        pds(j0, kb, false, st, dpt);
-        dqk(kt_l, kb, dpt);
-      }
-    } else if (!need_mask) {
-      f32x16 st[2], dpt[2];
-      sdp(kt_l, vt_l, 0, st[0], dpt[0]);
-#pragma unroll
-      for (int kb = 0; kb < KB; kb++) {
-        if (kb + 1 < KB) sdp(kt_l, vt_l, kb + 1, st[(kb + 1) & 1], dpt[(kb + 1) & 1]);
-        pds(j0, kb, false, st[kb & 1], dpt[kb & 1]);
-        dqk(kt_l, kb, dpt[kb & 1]);
-      }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KB; kb++) {
-        if (CAUSAL && j0 + 32 * kb > qw0 + 31 + off) continue;
-        f32x16 st, dpt;
-        sdp(kt_l, vt_l, kb, st, dpt);
-        pds(j0, kb, true, st, dpt);
-        dqk(kt_l, kb, dpt);
+      for (int cb = 0; cb < D / 32; cb++) {
+        const bf16x8 ka = join_bf16(ds_read_tr16(kk + toff[cb][0]), ds_read_tr16(kk + toff[cb][1]));
+        acc[cb] = mfma32(ka, sb, acc[cb]);
       }
     }
   };
+  auto compute = [&](int t, auto buf) {
+    block(t, buf, std::integral_constant<int, 0>{});
+    // keep the two blocks apart: overlapping them would need a second set of
+    // S^T / dP^T registers, more than a wave has at two waves per SIMD
+    __builtin_amdgcn_sched_barrier(0);
+    block(t, buf, std::integral_constant<int, 1>{});
+    static_assert(KB == 2, "two 32-key blocks per tile");
+  };
 
-  auto step = [&](int t, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
-                  char* __restrict__ vn) {
+  using c0 = std::integral_constant<int, 0>;
+  using c1 = std::integral_constant<int, 1>;
+  for (int t = 0; t < n_kt; t += 2) {
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_kt) issue(t + 1, kn, vn);
-    compute(t, kc, vc);
-  };
-  char* const b0 = smem;
-  char* const b1 = smem + 2 * TILE;
-  for (int t = 0; t < n_kt; t += 2) {
-    step(t, b0, b0 + TILE, b1, b1 + TILE);
+    if (t + 1 < n_kt) issue(t + 1, smem + TILE, smem + 3 * TILE);
+    compute(t, c0{});
     if (t + 1 >= n_kt) break;
-    step(t + 1, b1, b1 + TILE, b0, b0 + TILE);
+    wait_vmem();
+    __syncthreads();
+    if (t + 2 < n_kt) issue(t + 2, smem, smem + 2 * TILE);
+    compute(t + 1, c1{});
   }
 
   if (q_in) {
@@ -203,14 +183,20 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_Q_OCC) void bwd_dq_kernel(BwdArgs
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
-  constexpr int NW = 4;
+template <int D, bool CAUSAL, int NW>
+hipError_t launch_nw(const BwdArgs& a, hipStream_t s) {
   BwdArgs qa = a;
   qa.n_tiles = (a.Nq + NW * 32 - 1) / (NW * 32);
   qa.n_wgs = a.B * a.Hq * qa.n_tiles;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, ATTN_BWD_DQ_BN, CAUSAL>), dim3(qa.n_wgs), dim3(NW * 64), 0, s, qa);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(qa.n_wgs), dim3(NW * 64), 0, s, qa);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
+  // 8 waves (256 rows) per workgroup when that still gives 8 workgroups per CU
+  const bool big = (int64_t)a.B * a.Hq * ((a.Nq + 255) / 256) >= 8 * 256;
+  return big ? launch_nw<D, CAUSAL, 8>(a, s) : launch_nw<D, CAUSAL, 4>(a, s);
 }
 
 }  // namespace

@@ -54,7 +54,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_KV_OCC) void bwd_dkdv_kernel(BwdA
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];  // per stage: [Q | dO | records]
 
   const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
+  // the per-lane form on purpose: with the wave index made uniform the
+  // compiler specialises this kernel's branches and needs ~80 more registers
+  // (spilling in the non-causal instantiation)
+  const int wave = threadIdx.x >> 6;
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
