@@ -103,15 +103,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
 
-  // one 32-key block kb of tile t in buffer BUF
-  auto block = [&](int t, auto buf, auto kbc) {
-    constexpr int BUF = decltype(buf)::value;
+  // one 32-key block kb of tile t, whose K and V sit in kcur and vcur
+  auto block = [&](int t, auto kbc, const char* __restrict__ kcur, const char* __restrict__ vcur) {
     constexpr int kb = decltype(kbc)::value;
     const int j0 = t * BN + kb * 32;
     if (CAUSAL && j0 > qw0 + 31 + off) return;  // no key of the block visible to this wave
     const bool need_mask = (j0 + 32 > a.Nk) || (qw0 + 32 > a.Nq) || (CAUSAL && j0 + 31 > qw0 + off);
-    const char* kt = smem + BUF * TILE + kb * 32 * (D * 2);
-    const char* vt = smem + (2 + BUF) * TILE + kb * 32 * (D * 2);
+    const char* kt = kcur + kb * 32 * (D * 2);
+    const char* vt = vcur + kb * 32 * (D * 2);
     // S^T = K Q^T and dP^T = V dO^T: keys on M, this wave's queries on N
     f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
@@ -146,27 +145,29 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
       }
     }
   };
-  auto compute = [&](int t, auto buf) {
-    block(t, buf, std::integral_constant<int, 0>{});
+  auto compute = [&](int t, const char* __restrict__ kcur, const char* __restrict__ vcur) {
+    block(t, std::integral_constant<int, 0>{}, kcur, vcur);
     // keep the two blocks apart: overlapping them would need a second set of
     // S^T / dP^T registers, more than a wave has at two waves per SIMD
     __builtin_amdgcn_sched_barrier(0);
-    block(t, buf, std::integral_constant<int, 1>{});
+    block(t, std::integral_constant<int, 1>{}, kcur, vcur);
     static_assert(KB == 2, "two 32-key blocks per tile");
   };
 
-  using c0 = std::integral_constant<int, 0>;
-  using c1 = std::integral_constant<int, 1>;
+  // the restrict qualifiers tell the compiler the prefetch does not write
+  // the stage being read; without them it waits for the prefetch before the
+  // transposed K reads
+  auto step = [&](int t, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
+                  char* __restrict__ vn) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < n_kt) issue(t + 1, kn, vn);
+    compute(t, kc, vc);
+  };
   for (int t = 0; t < n_kt; t += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < n_kt) issue(t + 1, smem + TILE, smem + 3 * TILE);
-    compute(t, c0{});
+    step(t, smem, smem + 2 * TILE, smem + TILE, smem + 3 * TILE);
     if (t + 1 >= n_kt) break;
-    wait_vmem();
-    __syncthreads();
-    if (t + 2 < n_kt) issue(t + 2, smem, smem + 2 * TILE);
-    compute(t + 1, c1{});
+    step(t + 1, smem + TILE, smem + 3 * TILE, smem, smem + 2 * TILE);
   }
 
   if (q_in) {

@@ -57,12 +57,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int KB = KS / 32;                  // 32-key blocks per sub-tile
   static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly over the workgroup");
   static_assert(BN % KS == 0, "BN must be a multiple of 64");
-  static_assert(2 * TILE_BYTES <= 65536, "LDS offsets must fit the 16-bit immediate");
+  static_assert(TILE_BYTES <= 65536, "LDS offsets must fit the 16-bit immediate");
 
-  // buffers: [K0 | K1 | V0 | V1]; reads address K through koff and V through
-  // voff (which include the V0 base), the buffer, sub-tile, key block and row
-  // half through the immediate offset (at most 2 * TILE_BYTES - 16 rows)
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
+  // Two stages of one K and one V tile each; tile t uses stage t % 2.  Every
+  // tile buffer is its own LDS object: the compiler then proves that the
+  // prefetch into one stage does not alias the reads of the other (with
+  // offsets into one array it waits for the prefetch in flight before the
+  // transposed V reads).  Reads address K through koff and V through voff;
+  // the sub-tile, key block and row half go into the instructions' immediate
+  // offset.
+  __shared__ __attribute__((aligned(1024))) char k_st0[TILE_BYTES], k_st1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_st0[TILE_BYTES], v_st1[TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  if (n_tiles > 0) issue(0, smem, smem + 2 * TILE_BYTES);
+  if (n_tiles > 0) issue(0, k_st0, v_st0);
 
   // ---- Q fragments (B operand of S^T = K Q^T): row qw0 + l32, dims 16s + 8h .. +8
   bf16x8 qf[D / 16];
@@ -134,8 +139,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   for (int cb = 0; cb < D / 32; cb++)
 #pragma unroll
     for (int lh = 0; lh < 2; lh++)
-      voff[cb][lh] = 2 * TILE_BYTES +
-                     tile_off<D>(4 * h32 + ((lane & 15) >> 2) + 8 * lh, cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+      voff[cb][lh] = tile_off<D>(4 * h32 + ((lane & 15) >> 2) + 8 * lh, cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -144,12 +148,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   float l_run = 0.0f;     // this lane's share of the running sum
   const int qi = qw0 + l32;
 
-  // one 64-key sub-tile at key offset 64 * SUB of the tile in buffer BUF
-  auto compute_sub = [&](int t, auto buf, auto sub) {
-    constexpr int BUF = decltype(buf)::value;
+  // one 64-key sub-tile at key offset 64 * SUB of tile t, whose K and V sit
+  // in kcur and vcur
+  auto compute_sub = [&](int t, auto sub, const char* __restrict__ kcur, const char* __restrict__ vcur) {
     constexpr int SUB = decltype(sub)::value;
-    const char* kt = smem + BUF * TILE_BYTES + SUB * KS * (D * 2);
-    const char* vt = smem + BUF * TILE_BYTES + SUB * KS * (D * 2);  // + voff, which holds the V0 base
+    const char* kt = kcur + SUB * KS * (D * 2);
+    const char* vt = vcur + SUB * KS * (D * 2);
     const int j0 = t * BN + SUB * KS;
     // wave-level classification of the sub-tile
     if (j0 >= a.Nk) return;
@@ -253,28 +257,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       }
   };
 
-  auto compute = [&](int t, auto buf) {
-    compute_sub(t, buf, std::integral_constant<int, 0>{});
-    if constexpr (BN / KS > 1) compute_sub(t, buf, std::integral_constant<int, 1>{});
+  auto compute = [&](int t, const char* __restrict__ kcur, const char* __restrict__ vcur) {
+    compute_sub(t, std::integral_constant<int, 0>{}, kcur, vcur);
+    if constexpr (BN / KS > 1) compute_sub(t, std::integral_constant<int, 1>{}, kcur, vcur);
     static_assert(BN / KS <= 2, "at most two sub-tiles");
   };
 
-  // ---- one pipeline step: prefetch tile t+1 into the other buffers, compute
-  // tile t.  The prefetch writes only the other buffer pair, and each step's
-  // buffers are compile-time offsets, so the compiler can see the prefetch
-  // does not alias the tile being read.
-  using buf0 = std::integral_constant<int, 0>;
-  using buf1 = std::integral_constant<int, 1>;
+  // ---- one pipeline step: wait until tile t has landed, barrier, prefetch
+  // tile t+1 into the other stage, compute tile t.  kc, vc: the K and V
+  // tiles of this step's stage; kn, vn: the other stage.
+  auto step = [&](int t, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
+                  char* __restrict__ vn) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < n_tiles) issue(t + 1, kn, vn);
+    compute(t, kc, vc);
+  };
   for (int t = 0; t < n_tiles; t += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < n_tiles) issue(t + 1, smem + TILE_BYTES, smem + 3 * TILE_BYTES);
-    compute(t, buf0{});
+    step(t, k_st0, v_st0, k_st1, v_st1);
     if (t + 1 >= n_tiles) break;
-    wait_vmem();
-    __syncthreads();
-    if (t + 2 < n_tiles) issue(t + 2, smem, smem + 2 * TILE_BYTES);
-    compute(t + 1, buf1{});
+    step(t + 1, k_st1, v_st1, k_st0, v_st0);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
