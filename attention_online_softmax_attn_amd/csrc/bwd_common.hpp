@@ -30,10 +30,11 @@
 //
 // The dK/dV kernel runs one wave per SIMD (its K, V fragments and dK, dV
 // accumulators exceed half the register file), so its softmax-gradient VALU
-// work is overlapped with MFMA work inside each wave: the loop over 32-row
-// blocks is software-pipelined so that the contractions of block i+1 are
-// independent of, and issued around, the exponentials of block i.  The dQ
-// kernel fits two waves per SIMD, which overlap each other.
+// work is overlapped with MFMA work inside each wave: the 32-row blocks are
+// software-pipelined two deep (S/dP of block i+1 and dV/dK of block i-1 run
+// on the matrix core while the VALU turns S/dP of block i into P/dS), with
+// the instruction order fixed slot by slot.  The dQ kernel fits two waves
+// per SIMD, which overlap each other.
 #pragma once
 
 #include "device_common.hpp"
@@ -44,9 +45,14 @@
 #ifndef ATTN_BWD_KV_OCC
 #define ATTN_BWD_KV_OCC 1
 #endif
-// 1: software-pipeline the 32-row blocks of unmasked tiles (dK/dV kernel)
-#ifndef ATTN_BWD_PIPE
-#define ATTN_BWD_PIPE 1
+
+// dK/dV pipeline: LDS reads are issued this many contraction slots ahead
+#ifndef ATTN_BWD_LEAD
+#define ATTN_BWD_LEAD 8
+#endif
+// dK/dV pipeline: row records are read this many slots before first use
+#ifndef ATTN_BWD_REC_LEAD
+#define ATTN_BWD_REC_LEAD 6
 #endif
 
 #ifndef ATTN_BWD_BQ

@@ -34,10 +34,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
-  const int work = xcd_remap(blockIdx.x, a.n_wgs);
-  const int per_pair = a.g * a.n_tiles;
-  const int pair = work / per_pair;
-  const int rem = work % per_pair;
+  const WorkItem wi = lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_tiles);
+  const int pair = wi.pair;
+  const int rem = wi.sub;
   const int qt = CAUSAL ? (a.n_tiles - 1 - rem / a.g) : (rem / a.g);
   const int hq = (pair % a.Hkv) * a.g + rem % a.g;
   const int b = pair / a.Hkv;

@@ -1,6 +1,8 @@
 // Backward kernels of softmax attention on gfx950, part 1: the per-row
 // records and dK, dV (the formulas and the kernel split are stated in
 // bwd_common.hpp).
+#include <type_traits>
+
 #include "bwd_common.hpp"
 
 namespace attn {
@@ -61,9 +63,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_KV_OCC) void bwd_dkdv_kernel(BwdA
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
-  const int work = xcd_remap(blockIdx.x, a.n_wgs);
-  const int kt = work % a.n_tiles;  // causal: early key tiles are seen by the most queries, so they go first
-  const int pair = work / a.n_tiles;
+  // causal: early key tiles are seen by the most queries, so they go first
+  const WorkItem wi = lpt_order(blockIdx.x, a.B * a.Hkv, a.n_tiles);
+  const int kt = wi.sub;
+  const int pair = wi.pair;
   const int b = pair / a.Hkv;
   const int kvh = pair % a.Hkv;
   const int j0 = kt * (NW * 32);
@@ -129,84 +132,141 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_KV_OCC) void bwd_dkdv_kernel(BwdA
     }
   };
 
-  // S and dP of 32-row block nb: queries on M (row 32 nb + l32 of the tile), keys on N.
-  // All operand fragments are read from LDS before the contractions start, so
-  // the MFMAs issue back to back instead of each waiting for its own read.
-  auto sdp = [&](const char* st_l, int nb, f32x16& sa, f32x16& da) {
+  // ---- hand-ordered pipeline over the 32-row blocks of one tile.  Round nb
+  // (nb = -1 .. NB) issues the contractions S/dP of block nb + 1 and dV/dK of
+  // block nb - 1, alternating one of each kind per slot, and spreads the P/dS
+  // arithmetic of block nb over the slots, so that with one wave per SIMD the
+  // VALU work runs while the matrix core is busy.  Each slot also issues the
+  // LDS reads of the contraction LEAD slots ahead (across round boundaries)
+  // and, in the first slots of a round, the row records the next round
+  // needs, so a contraction rarely waits for its operands.  The scheduling
+  // barriers between slots keep the compiler from regrouping the slots.
+  auto run_tile = [&](const char* st_l, int i0, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
+    constexpr int SK = D / 16;     // contraction steps of S (and of dP); also dV (and dK) MFMAs per block
+    constexpr int NSLOT = 4 * SK;  // slots per round
+    constexpr int NG = (NB + 2) * NSLOT;
+    constexpr int LEAD = ATTN_BWD_LEAD;
+    static_assert(LEAD < NSLOT, "reads run at most one round ahead");
+    constexpr int CBN = D / 32;
+    constexpr int PER = NSLOT / 16;  // slots per P/dS element
     const char* qt_l = st_l;
     const char* dt_l = st_l + TILE;
-    bf16x8 qa[D / 16], oa[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; s++) {
-      const int off_b = (32 * nb + l32) * (D * 2) + (((2 * s + h32) ^ swl) << 4);
-      qa[s] = *(const bf16x8*)(qt_l + off_b);
-      oa[s] = *(const bf16x8*)(dt_l + off_b);
-    }
-    sa = f32x16{};
-    da = f32x16{};
-#pragma unroll
-    for (int s = 0; s < D / 16; s++) {
-      sa = mfma32(qa[s], kf[s], sa);
-      da = mfma32(oa[s], vf[s], da);
-    }
-  };
-
-  // P = 2^(s c - LSE2) and dS = P (dP - D) in place; rows 8(r/4) + 4h + r%4 of block nb
-  auto pds = [&](const char* st_l, int nb, int i0, bool mask, f32x16& sa, f32x16& da) {
     const float* rec = (const float*)(st_l + 2 * TILE);
-#pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) {
-      const int rl = 32 * nb + 8 * r4 + 4 * h32;  // first of 4 consecutive rows
-      const f32x4 x0 = *(const f32x4*)(rec + 2 * rl);
-      const f32x4 x1 = *(const f32x4*)(rec + 2 * rl + 4);
-      const float l2[4] = {x0[0], x0[2], x1[0], x1[2]};
-      const float dd[4] = {x0[1], x0[3], x1[1], x1[3]};
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int r = 4 * r4 + e;
-        float p = fast_exp2(__builtin_fmaf(sa[r], a.c, -l2[e]));
-        float ds = p * (da[r] - dd[e]);
-        if (mask) {
-          // selects, not products: a padding row's record may hold anything
-          const int i = i0 + rl + e;
-          bool ok = (i < a.Nq) && (jl < a.Nk);
-          if (CAUSAL) ok = ok && (jl <= i + off);
-          p = ok ? p : 0.0f;
-          ds = ok ? ds : 0.0f;
-        }
-        sa[r] = p;
-        da[r] = ds;
-      }
+    // mask of this lane's key jl over the rows i0 + 4h + c of the tile:
+    // visible iff lo <= c < hi with hi = Nq - i0 - 4h and, when causal,
+    // lo = jl - off - i0 - 4h (a key past Nk sees no row)
+    int m_lo = 0;
+    uint32_t m_span = 0;
+    if (MASK) {
+      const int base = i0 + 4 * h32;
+      const int hi = a.Nq - base;
+      int lo = CAUSAL ? jl - off - base : -(1 << 30);
+      if (jl >= a.Nk) lo = 1 << 30;
+      m_lo = lo;
+      m_span = hi > lo ? (uint32_t)(hi - lo) : 0u;
     }
-  };
+    f32x16 sa[2], da[2];
+    bf16x8 pa[2], sb[2];
+    bf16x8 qa[SK], oa[SK];
+    bf16x8 dob[2][CBN], qb[2][CBN];
+    f32x4 rx[8];  // row records of the block in P/dS: part q holds rows 8(q/2) + 4h + 2(q%2) .. +1
 
-  // dV += P^T dO, dK += dS^T Q over the 32 rows of block nb (dO and Q read
-  // transposed; all fragments of a 16-row half are read before its MFMAs)
-  auto dvdk = [&](const char* st_l, int nb, const f32x16& sa, const f32x16& da) {
-    const char* qt_l = st_l;
-    const char* dt_l = st_l + TILE;
-#pragma unroll
-    for (int hf = 0; hf < 2; hf++) {
-      const int tr = 32 * nb + 16 * hf + 4 * h32 + ((lane & 15) >> 2);
-      bf16x8 dob[D / 32], qb[D / 32];
-#pragma unroll
-      for (int cb = 0; cb < D / 32; cb++) {
+    // slot k of round nb: kind k % 4 (0: S, 1: dV, 2: dP, 3: dK), step k / 4
+    auto read_slot = [&](int nb, int k) {
+      const int st = k >> 2, kind = k & 3;
+      if ((kind == 0 || kind == 2) && nb + 1 < NB) {
+        const int off_b = (32 * (nb + 1) + l32) * (D * 2) + (((2 * st + h32) ^ swl) << 4);
+        if (kind == 0)
+          qa[st] = *(const bf16x8*)(qt_l + off_b);
+        else
+          oa[st] = *(const bf16x8*)(dt_l + off_b);
+      }
+      if ((kind == 1 || kind == 3) && nb >= 1) {
+        const int hf = st / CBN, cb = st % CBN;
+        const int tr = 32 * (nb - 1) + 16 * hf + 4 * h32 + ((lane & 15) >> 2);
         const int tc = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         const int o1 = tile_off<D>(tr, tc), o2 = tile_off<D>(tr + 8, tc);
-        dob[cb] = join_bf16(ds_read_tr16(dt_l + o1), ds_read_tr16(dt_l + o2));
-        qb[cb] = join_bf16(ds_read_tr16(qt_l + o1), ds_read_tr16(qt_l + o2));
+        if (kind == 1)
+          dob[hf][cb] = join_bf16(ds_read_tr16(dt_l + o1), ds_read_tr16(dt_l + o2));
+        else
+          qb[hf][cb] = join_bf16(ds_read_tr16(qt_l + o1), ds_read_tr16(qt_l + o2));
       }
-      bf16x8 pa, sb;
+    };
+    auto read_global = [&](int g) { read_slot(g / NSLOT - 1, g % NSLOT); };
+    auto read_rec = [&](int nb, int q) {
+      const int rl = 32 * nb + 8 * (q >> 1) + 4 * h32 + 2 * (q & 1);
+      rx[q] = *(const f32x4*)(rec + 2 * rl);
+    };
+    // part q of the records is first used at slot PER * (4 (q/2) + 2 (q%2))
+    // of a round; it is read REC_LEAD slots earlier (in the previous round
+    // when that is negative), so only a few parts are live at a time
+    constexpr int REC_LEAD = ATTN_BWD_REC_LEAD;
+    auto rec_first = [](int q) { return PER * (4 * (q >> 1) + 2 * (q & 1)); };
+    auto mfma_slot = [&](int nb, int k) {
+      const int st = k >> 2, kind = k & 3;
+      const int nxt = (nb + 1) & 1;
+      if (kind == 0 && nb + 1 < NB) sa[nxt] = mfma32(qa[st], kf[st], st == 0 ? f32x16{} : sa[nxt]);
+      if (kind == 2 && nb + 1 < NB) da[nxt] = mfma32(oa[st], vf[st], st == 0 ? f32x16{} : da[nxt]);
+      if ((kind == 1 || kind == 3) && nb >= 1) {
+        const int hf = st / CBN, cb = st % CBN;
+        if (kind == 1)
+          dv_acc[cb] = mfma32(pa[hf], dob[hf][cb], dv_acc[cb]);
+        else
+          dk_acc[cb] = mfma32(sb[hf], qb[hf][cb], dk_acc[cb]);
+      }
+    };
+    // P and dS of element r of block nb (row 8(r/4) + 4h + r%4)
+    auto pds_elem = [&](int nb, int r) {
+      const int cur = nb & 1;
+      const int r4 = r >> 2, e = r & 3;
+      const f32x4 x = rx[2 * r4 + (e >> 1)];
+      const float l2 = x[2 * (e & 1)], dd = x[2 * (e & 1) + 1];
+      float p = fast_exp2(__builtin_fmaf(sa[cur][r], a.c, -l2));
+      float ds = p * (da[cur][r] - dd);
+      if (MASK) {
+        // row i0 + 4h + c is visible to key jl iff lo <= c < lo + span;
+        // selects, not products: a padding row's record may hold anything
+        const int c = 32 * nb + 8 * r4 + e;
+        const bool ok = (uint32_t)(c - m_lo) < m_span;
+        p = ok ? p : 0.0f;
+        ds = ok ? ds : 0.0f;
+      }
+      sa[cur][r] = p;
+      da[cur][r] = ds;
+    };
+    auto pack_half = [&](int nb, int hf) {
+      const int cur = nb & 1;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        pa[e] = to_bf16(sa[8 * hf + e]);
-        sb[e] = to_bf16(da[8 * hf + e]);
+        pa[hf][e] = to_bf16(sa[cur][8 * hf + e]);
+        sb[hf][e] = to_bf16(da[cur][8 * hf + e]);
       }
+    };
+
 #pragma unroll
-      for (int cb = 0; cb < D / 32; cb++) {
-        dv_acc[cb] = mfma32(pa, dob[cb], dv_acc[cb]);
-        dk_acc[cb] = mfma32(sb, qb[cb], dk_acc[cb]);
+    for (int g = 0; g < LEAD; g++) read_global(g);
+#pragma unroll
+    for (int nb = -1; nb <= NB; nb++) {
+      const bool has_pds = nb >= 0 && nb < NB;
+#pragma unroll
+      for (int k = 0; k < NSLOT; k++) {
+        const int g = (nb + 1) * NSLOT + k;
+        if (g + LEAD < NG) read_global(g + LEAD);
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+          const int t = rec_first(q) - REC_LEAD;
+          if (t >= 0 && k == t && has_pds) read_rec(nb, q);
+          if (t < 0 && k == NSLOT + t && nb + 1 < NB) read_rec(nb + 1, q);
+        }
+        mfma_slot(nb, k);
+        if (has_pds && k % PER == 0) pds_elem(nb, k / PER);
+        // the dV/dK contractions of half 0 have all been issued before slot 4 CBN
+        if (has_pds && k == 4 * CBN) pack_half(nb, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (has_pds) pack_half(nb, 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -214,35 +274,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_KV_OCC) void bwd_dkdv_kernel(BwdA
     const int i0 = qtile_of(it) * BQ;
     if (CAUSAL && i0 + BQ - 1 + off < jw) return;  // no query of the tile sees this wave's keys
     const bool need_mask = (i0 + BQ > a.Nq) || (jw + 32 > a.Nk) || (CAUSAL && i0 + off < jw + 31);
-    if (!need_mask && !ATTN_BWD_PIPE) {
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) {
-        f32x16 sa, da;
-        sdp(st_l, nb, sa, da);
-        pds(st_l, nb, i0, false, sa, da);
-        dvdk(st_l, nb, sa, da);
-      }
-    } else if (!need_mask) {
-      // software pipeline over the 32-row blocks: the S/dP contractions of
-      // block nb + 1 are issued before the P/dS arithmetic of block nb
-      f32x16 sa[2], da[2];
-      sdp(st_l, 0, sa[0], da[0]);
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) {
-        if (nb + 1 < NB) sdp(st_l, nb + 1, sa[(nb + 1) & 1], da[(nb + 1) & 1]);
-        pds(st_l, nb, i0, false, sa[nb & 1], da[nb & 1]);
-        dvdk(st_l, nb, sa[nb & 1], da[nb & 1]);
-      }
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) {
-        if (CAUSAL && i0 + 32 * nb + 31 + off < jw) continue;
-        f32x16 sa, da;
-        sdp(st_l, nb, sa, da);
-        pds(st_l, nb, i0, true, sa, da);
-        dvdk(st_l, nb, sa, da);
-      }
-    }
+    if (need_mask)
+      run_tile(st_l, i0, std::true_type{});
+    else
+      run_tile(st_l, i0, std::false_type{});
   };
 
   // One step: wait until tile it has landed (with NS = 3, tile it + 1 may

@@ -149,4 +149,26 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
   return start + t;
 }
 
+// Launch index -> (pair, sub) for a grid of n_pairs * per_pair workgroups
+// whose sub 0 is the heaviest item of a pair and later subs are lighter.  The
+// dispatcher sends workgroup pid to XCD pid % 8 and starts the workgroups of
+// one XCD in order of pid / 8.  When the pairs split evenly over the XCDs,
+// XCD x takes pairs [x P/8, (x+1) P/8) (the workgroups of a pair share their
+// K/V or Q/dO reads in that XCD's L2) and starts them heaviest sub first
+// across all its pairs; otherwise the whole grid goes heaviest sub first.
+// Heaviest-first keeps long workgroups from starting last and running alone
+// at the end of a launch.  A bijection on [0, n_pairs * per_pair).
+struct WorkItem {
+  int pair, sub;
+};
+__device__ __forceinline__ WorkItem lpt_order(int pid, int n_pairs, int per_pair) {
+  constexpr int kXcd = 8;
+  if (n_pairs % kXcd == 0) {
+    const int ppx = n_pairs / kXcd;
+    const int x = pid % kXcd, t = pid / kXcd;
+    return {x * ppx + t % ppx, t / ppx};
+  }
+  return {pid % n_pairs, pid / n_pairs};
+}
+
 }  // namespace attn

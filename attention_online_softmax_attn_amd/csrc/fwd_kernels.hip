@@ -74,11 +74,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- work decomposition: (b, kv head, q tile desc., head in group), XCD-grouped
-  const int work = xcd_remap(blockIdx.x, a.n_wgs);
-  const int per_pair = a.g * a.n_qtiles;
-  const int pair = work / per_pair;
-  const int rem = work % per_pair;
+  // ---- work decomposition: (b, kv head) pair, then q tile (descending when
+  // causal) and head in group
+  const WorkItem wi = lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_qtiles);
+  const int pair = wi.pair;
+  const int rem = wi.sub;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
   const int hq = (pair % a.Hkv) * a.g + rem % a.g;
   const int b = pair / a.Hkv;
@@ -324,10 +324,9 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgsF32 a) {
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
-  const int work = xcd_remap(blockIdx.x, a.n_wgs);
-  const int per_pair = a.g * a.n_qtiles;
-  const int pair = work / per_pair;
-  const int rem = work % per_pair;
+  const WorkItem wi = lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_qtiles);
+  const int pair = wi.pair;
+  const int rem = wi.sub;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
   const int hq = (pair % a.Hkv) * a.g + rem % a.g;
   const int b = pair / a.Hkv;
