@@ -6,11 +6,14 @@ kernels on the current PyTorch stream.  There is no CPU path: if the library is
 not built, or a tensor is not on the GPU, these functions raise.
 
     attn_fwd(q, k, v, causal, scale)                  -> (o, lse)
+    attn_fwd_varlen(q, k, v, cu_q, cu_k, max_q, ...)  -> (o, lse)
     attn_decode_splitkv(q, k, v, scale, num_splits=0) -> (o, lse)
     attn_bwd(q, k, v, o, dout, lse, causal, scale)    -> (dq, dk, dv)
 
 Layouts are [B, H, N, d] contiguous (q/o/dout/dq with Hq heads, k/v/dk/dv with
-Hkv heads); lse is [B, Hq, Nq] fp32; gradients are fp32.  See include/attn.h.
+Hkv heads); lse is [B, Hq, Nq] fp32; gradients are fp32.  The variable-length
+forward takes packed [H, total, d] tensors and int32 sequence offsets.  See
+include/attn.h.
 """
 from __future__ import annotations
 
@@ -48,6 +51,8 @@ def lib() -> ctypes.CDLL:
     vp, i64, f32, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci, vp]
     L.attn_fwd.restype = ci
+    L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci, ci, vp]
+    L.attn_fwd_varlen.restype = ci
     L.attn_decode_num_splits.argtypes = [i64, i64, i64, i64, i64]
     L.attn_decode_num_splits.restype = ci
     L.attn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
@@ -120,6 +125,38 @@ def attn_fwd(q, k, v, causal: bool = False, scale=None, out=None, lse=None, want
                         d, _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream())
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
+    return o, (lse if want_lse else None)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False, scale=None,
+                    out=None, lse=None, want_lse: bool = True):
+    """Forward over a packed batch of variable-length sequences.
+
+    q [Hq, total_q, d], k/v [Hkv, total_k, d] (bf16); cu_seqlens_q/_k int32
+    [n_seqs + 1] device offsets of each sequence's rows; max_seqlen_q at least
+    the longest query length.  Returns (o [Hq, total_q, d], lse [Hq, total_q])."""
+    _check_dev(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [H, total, d]")
+    Hq, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    if k.shape[2] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of the same length n_seqs + 1")
+    n_seqs = cu_seqlens_q.shape[0] - 1
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if want_lse else None,
+                               _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), n_seqs, total_q, total_k, int(max_seqlen_q),
+                               Hq, Hkv, d, _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_varlen")
     return o, (lse if want_lse else None)
 
 

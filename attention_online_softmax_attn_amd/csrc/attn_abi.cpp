@@ -100,6 +100,25 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   return attn::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t n_seqs,
+                            int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t Hq, int64_t Hkv,
+                            int64_t d, float scale, int causal, attn_dtype dtype, void* stream) {
+  if (n_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0) return ATTN_ERR_INVALID;
+  attn_status st = check_common(n_seqs, Hq, Hkv, max_seqlen_q, total_k, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (total_q > ATTN_MAX_SEQ) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (n_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_OK;
+  if (!q || !o || !cu_seqlens_q || !cu_seqlens_k || (total_k > 0 && (!k || !v))) return ATTN_ERR_INVALID;
+  attn::FwdProblem p{q, k, v, o, lse, n_seqs, Hq, Hkv, max_seqlen_q, total_k, d, scale, causal ? 1 : 0, true};
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.tot_q = total_q;
+  p.tot_k = total_k;
+  return attn::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_decode_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d) {
   if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128)) return -1;
   return plan_splits(B, Hkv, Nk, 0).splits;

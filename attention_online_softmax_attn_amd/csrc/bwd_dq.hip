@@ -57,7 +57,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
   if (CAUSAL) kend = min(a.Nk, min(i0 + NW * 32, a.Nq) - 1 + off + 1);
   const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
 
-  auto issue = [&](int t, char* kt_l, char* vt_l) {
+  auto issue = [&](int t, char* kt_l, char* vt_l) __attribute__((always_inline)) {
     const int j0 = t * BN;
 #pragma unroll
     for (int n = 0; n < LOADS; n++) {
@@ -103,7 +103,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
   for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
 
   // one 32-key block kb of tile t, whose K and V sit in kcur and vcur
-  auto block = [&](int t, auto kbc, const char* __restrict__ kcur, const char* __restrict__ vcur) {
+  auto block = [&](int t, auto kbc, const char* __restrict__ kcur, const char* __restrict__ vcur)
+                   __attribute__((always_inline)) {
     constexpr int kb = decltype(kbc)::value;
     const int j0 = t * BN + kb * 32;
     if (CAUSAL && j0 > qw0 + 31 + off) return;  // no key of the block visible to this wave
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
       }
     }
   };
-  auto compute = [&](int t, const char* __restrict__ kcur, const char* __restrict__ vcur) {
+  auto compute = [&](int t, const char* __restrict__ kcur, const char* __restrict__ vcur)
+                     __attribute__((always_inline)) {
     block(t, std::integral_constant<int, 0>{}, kcur, vcur);
     // keep the two blocks apart: overlapping them would need a second set of
     // S^T / dP^T registers, more than a wave has at two waves per SIMD
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
   // the stage being read; without them it waits for the prefetch before the
   // transposed K reads
   auto step = [&](int t, const char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ kn,
-                  char* __restrict__ vn) {
+                  char* __restrict__ vn) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
     if (t + 1 < n_kt) issue(t + 1, kn, vn);

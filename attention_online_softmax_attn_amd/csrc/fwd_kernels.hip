@@ -45,6 +45,12 @@ struct FwdArgs {
   int B, Hq, Hkv, Nq, Nk, g;
   int n_qtiles, n_wgs;
   float c;  // scale * log2(e)
+  // packed variable-length batch (null for a dense one): sequence b holds
+  // query rows [cu_q[b], cu_q[b+1]) of q, o and lse and key rows
+  // [cu_k[b], cu_k[b+1]) of k and v; every head is [tot_q or tot_k, D]
+  const int* cu_q;
+  const int* cu_k;
+  int tot_q, tot_k;
 };
 
 template <int D, int NW, int BN, bool CAUSAL>
@@ -86,18 +92,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 
   const int i0 = qt * BM;
   const int qw0 = i0 + wave * 32;
-  const int off = a.Nk - a.Nq;  // causal: key j visible to query i iff j <= i + off
 
-  const size_t q_head = ((size_t)b * a.Hq + hq) * (size_t)a.Nq * D;
-  const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_head, (uint32_t)a.Nq * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)a.Nk * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)a.Nk * D * 2);
+  // this (batch or sequence, head) slice: its sizes and element offsets
+  int Nq = a.Nq, Nk = a.Nk;
+  size_t q_head, kv_head, lse_row;
+  if (a.cu_q != nullptr) {
+    // clamped, so that offsets that do not describe a packed batch cannot
+    // take a load outside q, k or v
+    const int q1 = min(a.cu_q[b + 1], a.tot_q), q0 = max(0, min(a.cu_q[b], q1));
+    const int k1 = min(a.cu_k[b + 1], a.tot_k), k0 = max(0, min(a.cu_k[b], k1));
+    Nq = q1 - q0;
+    Nk = k1 - k0;
+    q_head = ((size_t)hq * a.tot_q + q0) * D;
+    kv_head = ((size_t)kvh * a.tot_k + k0) * D;
+    lse_row = (size_t)hq * a.tot_q + q0;
+  } else {
+    q_head = ((size_t)b * a.Hq + hq) * (size_t)Nq * D;
+    kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)Nk * D;
+    lse_row = ((size_t)b * a.Hq + hq) * (size_t)Nq;
+  }
+  if (i0 >= Nq) return;  // the whole workgroup: a tile past this sequence's queries
+  const int off = Nk - Nq;  // causal: key j visible to query i iff j <= i + off
 
-  int kend = a.Nk;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_head, (uint32_t)Nq * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)Nk * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)Nk * D * 2);
+
+  int kend = Nk;
   if (CAUSAL) {
-    int last_row = min(i0 + BM, a.Nq) - 1;
-    kend = min(a.Nk, last_row + off + 1);
+    int last_row = min(i0 + BM, Nq) - 1;
+    kend = min(Nk, last_row + off + 1);
   }
   const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
@@ -156,8 +180,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     const char* vt = vcur + SUB * KS * (D * 2);
     const int j0 = t * BN + SUB * KS;
     // wave-level classification of the sub-tile
-    if (j0 >= a.Nk) return;
-    bool need_mask = (j0 + KS > a.Nk);
+    if (j0 >= Nk) return;
+    bool need_mask = (j0 + KS > Nk);
     if (CAUSAL) {
       if (j0 > qw0 + 31 + off) return;               // nothing visible to this wave
       if (j0 + KS - 1 > qw0 + off) need_mask = true;  // crosses this wave's diagonal
@@ -180,7 +204,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          bool ok = j < a.Nk;
+          bool ok = j < Nk;
           if (CAUSAL) ok = ok && (j <= qi + off);
           if (!ok) st[kb][r] = kNegInf;
         }
@@ -282,7 +306,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qi < a.Nq) {
+  if (qi < Nq) {
     __bf16* orow = a.o + q_head + (size_t)qi * D;
 #pragma unroll
     for (int cb = 0; cb < D / 32; cb++)
@@ -294,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
         *(bf16x4*)(orow + cb * 32 + 8 * g4 + 4 * h32) = w;
       }
     if (a.lse != nullptr && h32 == 0) {
-      a.lse[((size_t)b * a.Hq + hq) * a.Nq + qi] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+      a.lse[lse_row + qi] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
     }
   }
 }
@@ -431,6 +455,10 @@ hipError_t launch_bf16(const FwdProblem& p, hipStream_t s) {
   a.n_qtiles = (a.Nq + NW * 32 - 1) / (NW * 32);
   a.n_wgs = a.B * a.Hq * a.n_qtiles;
   a.c = p.scale * kLog2e;
+  a.cu_q = p.cu_q;
+  a.cu_k = p.cu_k;
+  a.tot_q = (int)p.tot_q;
+  a.tot_k = (int)p.tot_k;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, CAUSAL>), dim3(a.n_wgs), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }

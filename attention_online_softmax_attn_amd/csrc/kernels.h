@@ -19,6 +19,13 @@ struct FwdProblem {
   float scale;
   int causal;
   bool bf16;
+  // packed variable-length batch (bf16 only), null for a dense one: B is
+  // the number of sequences, Nq the longest query length (it sizes the
+  // grid), cu_q / cu_k the [B + 1] device offsets of each sequence's rows in
+  // the [H, tot_q or tot_k, d] tensors
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int64_t tot_q = 0, tot_k = 0;
 };
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
 

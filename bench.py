@@ -17,7 +17,10 @@ roofline = the prefill forward kernel (the step's dominant kernel) against the
            dense bf16 MFMA peak, timed with HIP events on its own stream
 cpu_baseline = the CPU oracle on a bounded sample of the same step's work
 
-Usage: python bench.py [--steps K] [--warmup W] [--no-cpu] [--paths fwd,decode,bwd]
+Opt-in path (not part of the default step): varlen = chunked prefill of a
+packed batch of 16 sequences (attn_fwd_varlen).
+
+Usage: python bench.py [--steps K] [--warmup W] [--no-cpu] [--paths fwd,decode,bwd[,varlen]]
 """
 from __future__ import annotations
 
@@ -38,6 +41,9 @@ METRIC = "attention fwd/bwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM pe
 PREFILL = dict(B=1, Hq=32, Hkv=8, N=44032, d=128, causal=True, seed=4)
 DECODE = dict(B=48, Hq=32, Hkv=8, L=4096, d=128, seed=3000 + 100 * 48 + 3)
 BACKWARD = dict(B=4, H=16, N=2048, d=128, causal=True, seed=5)
+# opt-in path (--paths ...,varlen): chunked prefill of 16 sequences, each
+# appending 512..2048 new tokens to a cached history of 0..4096 tokens
+VARLEN = dict(n=16, lq=(512, 2048), hist=(0, 4096), Hq=32, Hkv=8, d=128, seed=6, len_seed=7)
 
 
 CSRC = os.path.join(ROOT, "attention_online_softmax_attn_amd", "csrc")
@@ -80,6 +86,15 @@ def bwd_flops(B, Hq, Nq, Nk, d, causal):
     return 10.0 * B * Hq * Nq * Nk * d * (0.5 if causal else 1.0)
 
 
+def varlen_flops(lens_q, lens_k, Hq, d):
+    """4 d flop per visible (query, key) pair, causal per sequence (bottom-right)."""
+    pairs = 0
+    for lq, lk in zip(lens_q, lens_k):
+        off = lk - lq
+        pairs += sum(max(0, min(lk, i + off + 1)) for i in range(lq))
+    return 4.0 * Hq * d * pairs
+
+
 def decode_bytes(B, Hq, Hkv, L, d):
     return 2.0 * B * Hkv * L * d * 2 + 2.0 * B * Hq * d * 2 + B * Hq * 4
 
@@ -118,6 +133,15 @@ def setup(paths):
                                         with_dout=True)
         st["bwd_host"] = (q, k, v, do)
         st["bwd"] = (to_dev(q), to_dev(k), to_dev(v), to_dev(do))
+    if "varlen" in paths:
+        import torch
+
+        c = VARLEN
+        lens_q, lens_k = synth.chunked_prefill_lengths(c["len_seed"], c["n"], c["lq"], c["hist"])
+        q, k, v, cu_q, cu_k = synth.varlen_inputs(c["seed"], lens_q, lens_k, c["Hq"], c["Hkv"], c["d"], bf16=True)
+        st["varlen_lens"] = (lens_q, lens_k)
+        st["varlen"] = (to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda(),
+                        max(lens_q))
     return st
 
 
@@ -146,6 +170,9 @@ def run_gpu(paths, steps, warmup):
         f32 = dict(dtype=torch.float32, device="cuda")
         dev_out["bwd"] = (o, lse, torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32),
                           torch.empty(ws, dtype=torch.uint8, device="cuda"))
+    if "varlen" in paths:
+        q = st["varlen"][0]
+        dev_out["varlen"] = (torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
 
     def run_path(name):
@@ -157,12 +184,16 @@ def run_gpu(paths, steps, warmup):
             q, k, v = st["decode"]
             o, lse, ws = dev_out["decode"]
             am.attn_decode_splitkv(q, k, v, workspace=ws, out=o, lse=lse)
+        elif name == "varlen":
+            q, k, v, cq, ck, mq = st["varlen"]
+            o, lse = dev_out["varlen"]
+            am.attn_fwd_varlen(q, k, v, cq, ck, mq, causal=True, out=o, lse=lse)
         else:
             q, k, v, do = st["bwd"]
             o, lse, dq, dk, dv, ws = dev_out["bwd"]
             am.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
 
-    order = [p for p in ("fwd", "decode", "bwd") if p in paths]
+    order = [p for p in ("fwd", "decode", "bwd", "varlen") if p in paths]
     for _ in range(warmup):
         for p in order:
             run_path(p)
@@ -196,7 +227,8 @@ def cpu_baseline(st, paths, budget_s):
     flops = 0.0
     secs = 0.0
     parts = []
-    share = budget_s / max(1, len(paths))
+    # the oracle leg covers the default step's paths (not the opt-in varlen one)
+    share = budget_s / max(1, len([p for p in paths if p in ("fwd", "decode", "bwd")]))
     if "fwd" in paths:
         c = PREFILL
         q, k, v = st["fwd_host"]
@@ -315,6 +347,17 @@ def main():
         out_paths["backward"] = {"ms": round(t, 4), "ms_median": round(med(per["bwd"]), 4),
                                  "tflops": round(f / t / 1e9, 2), "frac_mfma": round(f / t / 1e9 / PEAK_BF16_TFLOPS, 4),
                                  "shape": "B=4 H=16 N=2048 d=128 causal"}
+        total_flops += f
+    if "varlen" in paths:
+        c = VARLEN
+        lens_q, lens_k = st["varlen_lens"]
+        f = varlen_flops(lens_q, lens_k, c["Hq"], c["d"])
+        t = sum(per["varlen"]) / len(per["varlen"])
+        out_paths["varlen_chunked_prefill"] = {
+            "ms": round(t, 4), "ms_median": round(med(per["varlen"]), 4), "tflops": round(f / t / 1e9, 2),
+            "frac_mfma": round(f / t / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "shape": f"{c['n']} sequences, new tokens {sum(lens_q)}, keys {sum(lens_k)}, Hq=32 Hkv=8 d=128, "
+                     "causal per sequence"}
         total_flops += f
     ms_step = sum(step_ms) / len(step_ms)
     value = total_flops / ms_step / 1e9

@@ -72,6 +72,33 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      void* stream);
 
 /*
+ * Forward prefill over a packed batch of variable-length sequences, and
+ * chunked prefill of new tokens against a KV history (the engine setting of
+ * the page "Tang Project Derives GPU Kernels via IR ...", section "Details":
+ * long prefills and many concurrent streams of unequal length).  Sequence s
+ * owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) and key rows
+ * [cu_seqlens_k[s], cu_seqlens_k[s+1]); its queries attend to its own keys
+ * only, with the causal rule above applied per sequence (Lk_s - Lq_s is the
+ * length of its history).
+ *   Layout   q, o : [Hq, total_q, d];  k, v : [Hkv, total_k, d];
+ *            lse  : [Hq, total_q] fp32 (may be NULL)
+ *   Offsets  cu_seqlens_q / cu_seqlens_k: device int32 arrays of n_seqs + 1
+ *            non-decreasing entries from 0 to total_q / total_k.  They are
+ *            read on the device only (the host never waits for them);
+ *            entries outside [0, total] are clamped, so no access leaves the
+ *            tensors.
+ *   Grid     max_seqlen_q must be at least every sequence's query length:
+ *            query rows past it are not written.
+ *   Types    ATTN_BF16 only (ATTN_F32 returns ATTN_ERR_UNSUPPORTED).
+ *   Sizes    n_seqs >= 0; total_q, total_k, max_seqlen_q <= ATTN_MAX_SEQ;
+ *            the other rules above.
+ */
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t n_seqs,
+                            int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t Hq, int64_t Hkv,
+                            int64_t d, float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
  * Split-KV decode: one query token per stream (Nq must be 1) against a KV
  * history of Nk keys.  Each kv head's keys are cut into num_splits chunks
  * (0 = automatic plan); every chunk yields a partial state (m, l, acc) for the

@@ -6,6 +6,8 @@ this package imports nothing from the GPU library: the two share no code.
 
 Contents
   attn_oracle.c  plain fp64 three-pass forward and analytic backward (C, OpenMP)
+  __init__.py    wrappers; fwd_varlen / fwd_varlen_rows compose the dense
+                 forward per sequence of a packed variable-length batch
   monoid.py      the online-softmax state (m, l, acc) and its combine rule
   brute.py       50-digit mpmath evaluation of the definition (no max shift)
 
@@ -130,6 +132,47 @@ def rowdot(q, k, v, dout, scale: float, causal: bool):
     if rc:
         raise ValueError(f"oracle_bwd_rowdot rejected its arguments ({rc})")
     return out
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool):
+    """Packed variable-length batch: sequence s is the dense problem on query
+    rows [cu_q[s], cu_q[s+1]) and key rows [cu_k[s], cu_k[s+1]) of every head
+    (its own keys only; causal alignment per sequence), solved by fwd above.
+    q [Hq, total_q, d], k, v [Hkv, total_k, d].  Returns (O [Hq, total_q, d],
+    LSE [Hq, total_q]) in fp64.  Rows outside every sequence stay NaN."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    Hq, tq, d = q.shape
+    o = np.full((Hq, tq, d), np.nan)
+    lse = np.full((Hq, tq), np.nan)
+    for s in range(len(cu_q) - 1):
+        a, b = int(cu_q[s]), int(cu_q[s + 1])
+        c, e = int(cu_k[s]), int(cu_k[s + 1])
+        if b == a:
+            continue
+        os_, ls_ = fwd(q[None, :, a:b], k[None, :, c:e], v[None, :, c:e], scale, causal)
+        o[:, a:b] = os_[0]
+        lse[:, a:b] = ls_[0]
+    return o, lse
+
+
+def fwd_varlen_rows(q, k, v, cu_q, cu_k, rows, scale: float, causal: bool):
+    """Like fwd_varlen on selected rows only.  rows: int array [n, 2] of (h, i)
+    with i a packed query row.  Returns (O [n, d], LSE [n])."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    rows = np.asarray(rows, np.int64).reshape(-1, 2)
+    cu_q = np.asarray(cu_q, np.int64)
+    seq = np.searchsorted(cu_q, rows[:, 1], side="right") - 1
+    o = np.empty((rows.shape[0], q.shape[2]))
+    lse = np.empty(rows.shape[0])
+    for s in np.unique(seq):
+        sel = np.nonzero(seq == s)[0]
+        a, b = int(cu_q[s]), int(cu_q[s + 1])
+        c, e = int(cu_k[s]), int(cu_k[s + 1])
+        local = np.stack([np.zeros(len(sel), np.int64), rows[sel, 0], rows[sel, 1] - a], axis=1)
+        os_, ls_ = fwd_rows(q[None, :, a:b], k[None, :, c:e], v[None, :, c:e], local, scale, causal)
+        o[sel] = os_
+        lse[sel] = ls_
+    return o, lse
 
 
 def num_threads() -> int:

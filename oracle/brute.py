@@ -86,3 +86,35 @@ def fd_grads(q, k, v, dout, scale: float, causal: bool, h: str = "1e-20"):
                 g[idx] = float((lp - lm) / (2 * step))
             grads.append(g)
     return tuple(grads)
+
+
+def brute_fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool):
+    """Packed variable-length batch at 50 digits, read straight off the packed
+    rows: query row i of sequence s (cu_q[s] <= i < cu_q[s+1]) sees key row j
+    iff cu_k[s] <= j < cu_k[s+1] and, when causal,
+    j - cu_k[s] <= (i - cu_q[s]) + (len_k(s) - len_q(s)).
+    q [Hq, total_q, d], k, v [Hkv, total_k, d]; returns float64 (O, LSE)."""
+    q, k, v = np.asarray(q, np.float64), np.asarray(k, np.float64), np.asarray(v, np.float64)
+    Hq, tq, d = q.shape
+    Hkv, tk = k.shape[0], k.shape[1]
+    g = Hq // Hkv
+    o = np.zeros((Hq, tq, d))
+    lse = np.full((Hq, tq), -np.inf)
+    with mpmath.workdps(DPS):
+        sc = mpmath.mpf(scale)
+        for h in range(Hq):
+            kv = h // g
+            for i in range(tq):
+                s = max(t for t in range(len(cu_q) - 1) if cu_q[t] <= i)
+                lq, lk = cu_q[s + 1] - cu_q[s], cu_k[s + 1] - cu_k[s]
+                js = [j for j in range(tk) if cu_k[s] <= j < cu_k[s + 1]
+                      and (not causal or j - cu_k[s] <= (i - cu_q[s]) + (lk - lq))]
+                if not js:
+                    continue
+                e = {j: mpmath.exp(sc * mpmath.fsum(mpmath.mpf(float(q[h, i, c])) * mpmath.mpf(float(k[kv, j, c]))
+                                                    for c in range(d))) for j in js}
+                z = mpmath.fsum(e.values())
+                for c in range(d):
+                    o[h, i, c] = float(mpmath.fsum(e[j] * mpmath.mpf(float(v[kv, j, c])) for j in js) / z)
+                lse[h, i] = float(mpmath.log(z))
+    return o, lse

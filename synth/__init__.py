@@ -88,3 +88,26 @@ def sample_rows(seed: int, n: int, B: int, Hq: int, Nq: int, forced_i=()) -> np.
             seen.add(t)
             rows.append(t)
     return np.array(rows[:n], np.int64)
+
+
+def offsets(lengths) -> np.ndarray:
+    """Row offsets of a packed batch: int32 [n + 1], 0 then the running sums."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, np.int64))]).astype(np.int32)
+
+
+def varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, d: int, bf16: bool):
+    """Packed variable-length batch: Q [Hq, sum(lens_q), d], K, V [Hkv, sum(lens_k), d]
+    drawn in that order, and the int32 offsets cu_q, cu_k."""
+    cu_q, cu_k = offsets(lens_q), offsets(lens_k)
+    q, k, v = normal(seed, [(Hq, int(cu_q[-1]), d), (Hkv, int(cu_k[-1]), d), (Hkv, int(cu_k[-1]), d)], bf16)
+    return q, k, v, cu_q, cu_k
+
+
+def chunked_prefill_lengths(seed: int, n: int, lq_range, history_range):
+    """Lengths of n sequences that append lq new tokens to a history of h
+    cached ones: lens_q = lq, lens_k = h + lq, each uniform in its range
+    (inclusive) from a generator separate from the data's."""
+    rng = np.random.default_rng(seed)
+    lq = rng.integers(lq_range[0], lq_range[1] + 1, size=n)
+    h = rng.integers(history_range[0], history_range[1] + 1, size=n)
+    return [int(x) for x in lq], [int(x + y) for x, y in zip(h, lq)]

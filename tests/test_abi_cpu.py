@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_decode_splitkv", "attn_bwd", "attn_decode_workspace_bytes",
+    for n in ("attn_fwd", "attn_fwd_varlen", "attn_decode_splitkv", "attn_bwd", "attn_decode_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_decode_num_splits", "attn_strerror"):
         assert n in names
 
@@ -89,6 +89,44 @@ def test_empty_outputs_launch_nothing():
     # B = 0 or Nq = 0: nothing to write, accepted even with null pointers
     assert fwd(q=NUL, k=NUL, v=NUL, o=NUL, lse=NUL, B=0) == am.ATTN_OK
     assert fwd(q=NUL, k=NUL, v=NUL, o=NUL, lse=NUL, Nq=0) == am.ATTN_OK
+
+
+def fwd_varlen(q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, n=3, tq=300, tk=500, maxq=128, Hq=4, Hkv=2, d=128,
+               scale=0.088, causal=1, dt=am.ATTN_BF16):
+    return am.lib().attn_fwd_varlen(q, k, v, o, lse, cq, ck, n, tq, tk, maxq, Hq, Hkv, d, scale, causal, dt, None)
+
+
+@no_gpu
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(q=NUL), am.ATTN_ERR_INVALID),
+        (dict(o=NUL), am.ATTN_ERR_INVALID),
+        (dict(cq=NUL), am.ATTN_ERR_INVALID),
+        (dict(ck=NUL), am.ATTN_ERR_INVALID),
+        (dict(k=NUL), am.ATTN_ERR_INVALID),
+        (dict(n=-1), am.ATTN_ERR_INVALID),
+        (dict(tq=-1), am.ATTN_ERR_INVALID),
+        (dict(tk=-5), am.ATTN_ERR_INVALID),
+        (dict(maxq=-1), am.ATTN_ERR_INVALID),
+        (dict(Hq=3), am.ATTN_ERR_INVALID),
+        (dict(scale=0.0), am.ATTN_ERR_INVALID),
+        (dict(dt=9), am.ATTN_ERR_INVALID),
+        (dict(dt=am.ATTN_F32), am.ATTN_ERR_UNSUPPORTED),
+        (dict(d=96), am.ATTN_ERR_UNSUPPORTED),
+        (dict(tq=(1 << 24) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(tk=(1 << 24) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(maxq=(1 << 24) + 1), am.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_fwd_varlen_rejects(kw, code):
+    assert fwd_varlen(**kw) == code
+
+
+@no_gpu
+def test_fwd_varlen_empty_launches_nothing():
+    for kw in (dict(n=0), dict(tq=0), dict(maxq=0)):
+        assert fwd_varlen(q=NUL, k=NUL, v=NUL, o=NUL, lse=NUL, cq=NUL, ck=NUL, **kw) == am.ATTN_OK
 
 
 def dec(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scale=0.088, splits=0, ws=P,
