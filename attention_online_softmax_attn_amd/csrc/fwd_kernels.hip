@@ -82,7 +82,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 
   // ---- work decomposition: (b, kv head) pair, then q tile (descending when
   // causal) and head in group
-  const WorkItem wi = lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_qtiles);
+  // A packed batch's sequences differ in length, so the XCD-local order
+  // (which gives each XCD whole sequences) would leave some XCDs with far
+  // more work than others: there every XCD gets a share of every sequence.
+  const WorkItem wi = (a.cu_q != nullptr)
+                          ? WorkItem{(int)(blockIdx.x % (a.B * a.Hkv)), (int)(blockIdx.x / (a.B * a.Hkv))}
+                          : lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_qtiles);
   const int pair = wi.pair;
   const int rem = wi.sub;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
