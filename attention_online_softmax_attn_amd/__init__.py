@@ -8,6 +8,7 @@ not built, or a tensor is not on the GPU, these functions raise.
     attn_fwd(q, k, v, causal, scale)                  -> (o, lse)
     attn_fwd_varlen(q, k, v, cu_q, cu_k, max_q, ...)  -> (o, lse)
     attn_decode_splitkv(q, k, v, scale, num_splits=0) -> (o, lse)
+    attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, ...) -> (o, lse)
     attn_bwd(q, k, v, o, dout, lse, causal, scale)    -> (dq, dk, dv)
 
 Layouts are [B, H, N, d] contiguous (q/o/dout/dq with Hq heads, k/v/dk/dv with
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci, vp, sz, ci, vp]
     L.attn_decode_splitkv.restype = ci
+    L.attn_decode_splitkv_fp8.argtypes = [vp] * 7 + [i64] * 6 + [f32, ci, vp, sz, vp]
+    L.attn_decode_splitkv_fp8.restype = ci
     L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, vp, sz, ci, vp]
@@ -185,6 +188,39 @@ def attn_decode_splitkv(q, k, v, scale=None, num_splits: int = 0, workspace=None
                                    _dtype_code(q), _stream())
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_splitkv")
+    return o, (lse if want_lse else None)
+
+
+def attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, scale=None, num_splits: int = 0, workspace=None, out=None,
+                            lse=None, want_lse: bool = True):
+    """Split-KV decode over an FP8 KV cache.  q bf16 [B, Hq, 1, d]; k8, v8 uint8
+    OCP E4M3 codes [B, Hkv, Nk, d]; k_scale, v_scale fp32 [Hkv] (value = scale *
+    code).  Returns (o bf16 [B, Hq, 1, d], lse)."""
+    _check_dev(q, k8, v8, k_scale, v_scale, out, lse, workspace)
+    if q.dim() != 4 or k8.dim() != 4 or v8.shape != k8.shape:
+        raise ValueError("q must be [B, Hq, 1, d] and k8, v8 [B, Hkv, Nk, d]")
+    if k8.dtype != torch.uint8 or v8.dtype != torch.uint8:
+        raise TypeError("k8 and v8 must hold uint8 E4M3 codes")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k8.shape[1], k8.shape[2]
+    if k8.shape[0] != B or k8.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k8 {tuple(k8.shape)}")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32 or k_scale.numel() != Hkv or v_scale.numel() != Hkv:
+        raise ValueError("k_scale and v_scale must be fp32 with one value per kv head")
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_splitkv_fp8(_ptr(q), _ptr(k8), _ptr(v8), _ptr(k_scale), _ptr(v_scale), _ptr(o),
+                                       _ptr(lse) if want_lse else None, B, Hq, Hkv, Nq, Nk, d, _scale(scale, d),
+                                       int(num_splits), _ptr(workspace), ws_bytes, _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_splitkv_fp8")
     return o, (lse if want_lse else None)
 
 

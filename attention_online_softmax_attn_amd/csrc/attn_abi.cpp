@@ -132,11 +132,14 @@ size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N
   return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
-attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                                int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
-                                int num_splits, void* workspace, size_t workspace_bytes, attn_dtype dtype,
-                                void* stream) {
-  (void)causal;  // one bottom-right-aligned query sees every key
+}  // extern "C"
+
+namespace {
+
+attn_status decode_common(const void* q, const void* k, const void* v, const float* k_scale, const float* v_scale,
+                          bool fp8, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                          int64_t d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                          attn_dtype dtype, void* stream) {
   attn_status st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (num_splits < 0) return ATTN_ERR_INVALID;
@@ -145,6 +148,7 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
   if (Hq / Hkv > 32) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (!q || !o || (Nk > 0 && (!k || !v))) return ATTN_ERR_INVALID;
+  if (fp8 && Nk > 0 && (!k_scale || !v_scale)) return ATTN_ERR_INVALID;
   SplitPlan sp = plan_splits(B, Hkv, Nk, num_splits);
   attn::DecodeProblem p{};
   p.q = q;
@@ -167,7 +171,34 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
     p.part_acc = (float*)workspace;
     p.part_ml = (float*)((char*)workspace + align256(rows * d * sizeof(float)));
   }
+  if (fp8 && Nk > 0) {
+    p.k8 = (const uint8_t*)k;
+    p.v8 = (const uint8_t*)v;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+  }
   return attn::launch_decode(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                                int num_splits, void* workspace, size_t workspace_bytes, attn_dtype dtype,
+                                void* stream) {
+  (void)causal;  // one bottom-right-aligned query sees every key
+  return decode_common(q, k, v, nullptr, nullptr, false, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits, workspace,
+                       workspace_bytes, dtype, stream);
+}
+
+attn_status attn_decode_splitkv_fp8(const void* q, const void* k, const void* v, const float* k_scale,
+                                    const float* v_scale, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                                    int64_t Nq, int64_t Nk, int64_t d, float scale, int num_splits, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return decode_common(q, k, v, k_scale, v_scale, true, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits, workspace,
+                       workspace_bytes, ATTN_BF16, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d) {

@@ -28,7 +28,10 @@ namespace attn {
 namespace {
 
 constexpr float kTau = 8.0f;
-constexpr int kWaves = 4;
+#ifndef ATTN_DECODE_WAVES
+#define ATTN_DECODE_WAVES 4
+#endif
+constexpr int kWaves = ATTN_DECODE_WAVES;
 
 struct DecArgs {
   const __bf16* q;
@@ -41,6 +44,12 @@ struct DecArgs {
   int B, Hq, Hkv, Nk, g;
   int S, chunk, n_wgs;
   float c;
+  // FP8 KV cache: k8, v8 hold OCP E4M3 codes; kv head h's values are
+  // k_scale[h] * code and v_scale[h] * code
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 template <int D>
@@ -221,6 +230,212 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-KV decode over an FP8 (OCP E4M3) KV cache with a scale per kv head.
+// Same decomposition and fold as the bf16 kernel; K and V move HBM -> LDS as
+// bytes (half the traffic), four stages per wave (three tiles in flight, the
+// same LDS as the bf16 kernel's two), and are widened to bf16 in registers
+// just before the MFMAs, which is exact.  The K scale folds into the exponent
+// scale and the V scale into the accumulator, so the arithmetic after the
+// loads is the bf16 kernel's.
+//   K (A operand of S^T = K Q^T): lane l reads bytes 16 s + 8 h .. +8 of key
+//   row l % 32 (h = l / 32).
+//   V^T (A operand of O^T += V^T P^T): one transposed byte read per MFMA; the
+//   rows each lane addresses are chosen so that the keys land in the order
+//   P^T uses (key slot 8 h + b of a 16-key half is key 4 h + b % 4 + 8 (b / 4)).
+// LDS tiles are [32 keys][D bytes] with 16-byte chunk c of row r stored at
+// chunk c ^ (r % (D / 16)).
+template <int D>
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_fp8_kernel(DecArgs a) {
+  constexpr int BN = kDecodeTile;
+  constexpr int TILE = BN * D;           // bytes of one K or V tile
+  constexpr int NST = 4;                 // stages per wave
+  constexpr int STAGE = 2 * TILE;        // K then V
+  constexpr int CPR = D / 16;            // 16-byte chunks per row
+  constexpr int LOADS = BN * CPR / 64;   // per lane per K (or V) tile
+  constexpr int VMT = 2 * LOADS;         // loads per wave per tile
+  static_assert(BN == 32, "one 32-key MFMA block per tile");
+  static_assert(LOADS * 64 == BN * CPR, "tile must split evenly over a wave");
+  static_assert(kWaves * NST * STAGE >= kWaves * 32 * D * 4 + 2 * kWaves * 32 * 4, "fold area fits the tiles");
+  __shared__ __attribute__((aligned(1024))) char smem[kWaves * NST * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int h32 = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int work = xcd_remap(blockIdx.x, a.n_wgs);
+  const int split = work % a.S;
+  const int pair = work / a.S;
+  const int b = pair / a.Hkv;
+  const int kvh = pair % a.Hkv;
+
+  const int k0 = split * a.chunk;
+  const int k1 = min(a.Nk, k0 + a.chunk);
+  const int n_tiles = k1 > k0 ? (k1 - k0 + BN - 1) / BN : 0;
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+
+  const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k8 + kv_head, (uint32_t)a.Nk * D);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v8 + kv_head, (uint32_t)a.Nk * D);
+  const size_t q_grp = ((size_t)b * a.Hq + (size_t)kvh * a.g) * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_grp, (uint32_t)a.g * D * 2);
+  const float c = a.c * a.k_scale[kvh];
+  const float vscale = a.v_scale[kvh];
+
+  char* wbase = smem + wave * NST * STAGE;
+  auto stage_of = [&](int i) { return wbase + (i % NST) * STAGE; };
+
+  auto issue = [&](int i) {
+    char* kt = stage_of(i);
+    char* vt = kt + TILE;
+    const int j0 = k0 + (wave + kWaves * i) * BN;
+#pragma unroll
+    for (int n = 0; n < LOADS; n++) {
+      const int p = n * 64 + lane;
+      const int r = p / CPR;
+      const int cc = (p % CPR) ^ (r % CPR);
+      const uint32_t src = (uint32_t)((j0 + r) * D + cc * 16);
+      buf_load_lds16(rk, src, (lds_void*)(kt + n * 1024));
+      buf_load_lds16(rv, src, (lds_void*)(vt + n * 1024));
+    }
+  };
+
+  // tile 0, this wave's queries, then the other tiles in flight: each wait
+  // below counts only tile loads issued after the tile it waits for
+  if (my_tiles > 0) issue(0);
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; s++)
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)((l32 * D + 16 * s + 8 * h32) * 2)));
+  for (int i = 1; i < NST - 1 && i < my_tiles; i++) issue(i);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
+  float m_run = kNegInf, l_run = 0.0f;
+
+  // lane-constant byte offsets: K (row l32, chunk s, half h32); V^T (rows and
+  // columns of the transposed read for 16-key half hf and d block cb)
+  const int g16 = lane >> 4, u = lane & 15;
+  auto k_off = [&](int s) { return l32 * D + (((s ^ (l32 % CPR)) << 4)) + 8 * h32; };
+  auto v_off = [&](int hf, int cb) {
+    const int row = 16 * hf + 4 * (g16 >> 1) + ((u >> 1) & 3) + 8 * (u >> 3);
+    const int chunk = 2 * cb + (g16 & 1);
+    return row * D + ((chunk ^ (row % CPR)) << 4) + 8 * (u & 1);
+  };
+
+  auto compute = [&](int i, const char* kt, const char* vt) {
+    const int j0 = k0 + (wave + kWaves * i) * BN;
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; s++) {
+      const i32x2 w = *(const i32x2*)(kt + k_off(s));
+      st = mfma32(fp8x8_to_bf16(w), qf[s], st);
+    }
+    if (j0 + BN > k1) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int j = j0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        if (j >= k1) st[r] = kNegInf;
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[r]);
+    mx = halves_max(mx) * c;
+    const bool grow = mx > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2(m_run - mx) : 1.0f;
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[cb][r] *= alpha;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      st[r] = fast_exp2(__builtin_fmaf(st[r], c, -m_use));
+      l_run += st[r];
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; e++) pb[e] = to_bf16(st[8 * hf + e]);
+#pragma unroll
+      for (int cb = 0; cb < D / 32; cb++)
+        acc[cb] = mfma32(fp8x8_to_bf16(ds_read_tr8(vt + v_off(hf, cb))), pb, acc[cb]);
+    }
+  };
+
+  for (int i = 0; i < my_tiles; i++) {
+    const int ahead = min(NST - 2, my_tiles - 1 - i);  // younger tiles already in flight
+    if (ahead >= 2)
+      wait_vmem_n<2 * VMT>();
+    else if (ahead == 1)
+      wait_vmem_n<VMT>();
+    else
+      wait_vmem();
+    // the stage of tile i + NST - 1 was tile i - 1's, whose reads are done
+    if (i + NST - 1 < my_tiles) issue(i + NST - 1);
+    const char* kt = stage_of(i);
+    compute(i, kt, kt + TILE);
+  }
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[cb][r] *= vscale;
+
+  // ---- fold the wave states: the monoid rule, through LDS
+  const float l_tot = halves_sum(l_run);
+  __syncthreads();  // every wave is done with its tile buffers
+  float* f_acc = (float*)smem;           // [kWaves][32][D]
+  float* f_m = f_acc + kWaves * 32 * D;  // [kWaves][32]
+  float* f_l = f_m + kWaves * 32;        // [kWaves][32]
+  if (l32 < a.g) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        f_acc[(wave * 32 + l32) * D + cb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3)] = acc[cb][r];
+    if (h32 == 0) {
+      f_m[wave * 32 + l32] = m_run;
+      f_l[wave * 32 + l32] = l_tot;
+    }
+  }
+  __syncthreads();
+  const int total = a.g * D;
+  for (int e = threadIdx.x; e < total; e += kWaves * 64) {
+    const int qh = e / D, col = e % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, f_m[w * 32 + qh]);
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+      const float mw = f_m[w * 32 + qh];
+      const float f = (mw == kNegInf) ? 0.0f : fast_exp2(mw - M);
+      L += f * f_l[w * 32 + qh];
+      A += f * f_acc[(w * 32 + qh) * D + col];
+    }
+    const int hq = kvh * a.g + qh;
+    const size_t row = (size_t)b * a.Hq + hq;
+    if (a.S == 1) {
+      a.o[row * D + col] = to_bf16(L > 0.0f ? A / L : 0.0f);
+      if (col == 0 && a.lse != nullptr) a.lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    } else {
+      a.part_acc[(row * a.S + split) * D + col] = A;
+      if (col == 0) {
+        a.part_ml[(row * a.S + split) * 2 + 0] = M;
+        a.part_ml[(row * a.S + split) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
 // Fold num_splits partial states per (b, query head).  One wave per row.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
@@ -267,7 +482,14 @@ hipError_t launch(const DecodeProblem& p, hipStream_t s) {
   a.chunk = p.chunk;
   a.n_wgs = a.B * a.Hkv * a.S;
   a.c = p.scale * kLog2e;
-  hipLaunchKernelGGL((decode_partial_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
+  a.k8 = p.k8;
+  a.v8 = p.v8;
+  a.k_scale = p.k_scale;
+  a.v_scale = p.v_scale;
+  if (p.k8 != nullptr)
+    hipLaunchKernelGGL((decode_partial_fp8_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.S == 1) return e;
   const int rows = a.B * a.Hq;

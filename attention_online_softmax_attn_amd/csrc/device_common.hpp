@@ -88,6 +88,26 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_byte_ptr) {
       (lds_s16x4*)(__attribute__((address_space(3))) char*)(lds_byte_ptr));
 }
 
+// Transposed 8-bit LDS read.  Within each group of 16 lanes, lane t receives
+// byte (t % 8) of the 8-byte words addressed by lanes 2b + t / 8 of the group,
+// b = 0 .. 7, as its bytes b (measured on gfx950).
+__device__ __forceinline__ i32x2 ds_read_tr8(const char* lds_byte_ptr) {
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(__attribute__((address_space(3))) char*)(lds_byte_ptr));
+}
+
+// Eight OCP FP8 E4M3 values (bytes 0..7 of w) -> bf16, exactly (every E4M3
+// value is a bf16 value; gfx950's conversion decodes the OCP format, measured
+// on all 256 codes).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 __device__ __forceinline__ bf16x8 join_bf16(s16x4 lo, s16x4 hi) {
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
   s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

@@ -41,6 +41,12 @@ struct DecodeProblem {
   int chunk;       // keys per split, a multiple of the kernel's key tile
   float* part_acc; // [B, Hq, num_splits, d] fp32 (unused when num_splits == 1)
   float* part_ml;  // [B, Hq, num_splits, 2] fp32 (running max in log2 units, sum)
+  // FP8 KV cache (null for bf16 k, v): OCP E4M3 codes [B, Hkv, Nk, d] and a
+  // fp32 scale per kv head for each of K and V
+  const uint8_t* k8 = nullptr;
+  const uint8_t* v8 = nullptr;
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
 };
 // Keys per decode tile; split chunks are whole multiples of it.
 constexpr int kDecodeTile = 32;

@@ -17,10 +17,11 @@ roofline = the prefill forward kernel (the step's dominant kernel) against the
            dense bf16 MFMA peak, timed with HIP events on its own stream
 cpu_baseline = the CPU oracle on a bounded sample of the same step's work
 
-Opt-in path (not part of the default step): varlen = chunked prefill of a
-packed batch of 16 sequences (attn_fwd_varlen).
+Opt-in paths (not part of the default step): varlen = chunked prefill of a
+packed batch of 16 sequences (attn_fwd_varlen); decode_fp8 = the decode shape
+over an FP8 E4M3 KV cache (attn_decode_splitkv_fp8).
 
-Usage: python bench.py [--steps K] [--warmup W] [--no-cpu] [--paths fwd,decode,bwd[,varlen]]
+Usage: python bench.py [--steps K] [--warmup W] [--no-cpu] [--paths fwd,decode,bwd[,varlen][,decode_fp8]]
 """
 from __future__ import annotations
 
@@ -95,8 +96,8 @@ def varlen_flops(lens_q, lens_k, Hq, d):
     return 4.0 * Hq * d * pairs
 
 
-def decode_bytes(B, Hq, Hkv, L, d):
-    return 2.0 * B * Hkv * L * d * 2 + 2.0 * B * Hq * d * 2 + B * Hq * 4
+def decode_bytes(B, Hq, Hkv, L, d, kv_bytes_per_elem=2):
+    return 2.0 * B * Hkv * L * d * kv_bytes_per_elem + 2.0 * B * Hq * d * 2 + B * Hq * 4
 
 
 def decode_flops(B, Hq, L, d):
@@ -133,6 +134,13 @@ def setup(paths):
                                         with_dout=True)
         st["bwd_host"] = (q, k, v, do)
         st["bwd"] = (to_dev(q), to_dev(k), to_dev(v), to_dev(do))
+    if "decode_fp8" in paths:
+        import torch
+
+        c = DECODE
+        q, k8, v8, ks, vs = synth.fp8_kv_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["L"], c["d"])
+        st["decode_fp8"] = (to_dev(q), torch.from_numpy(k8).cuda(), torch.from_numpy(v8).cuda(),
+                            torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda())
     if "varlen" in paths:
         import torch
 
@@ -170,6 +178,12 @@ def run_gpu(paths, steps, warmup):
         f32 = dict(dtype=torch.float32, device="cuda")
         dev_out["bwd"] = (o, lse, torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32),
                           torch.empty(ws, dtype=torch.uint8, device="cuda"))
+    if "decode_fp8" in paths:
+        q = st["decode_fp8"][0]
+        c = DECODE
+        ws = am.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], 0)
+        dev_out["decode_fp8"] = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"),
+                                 torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda"))
     if "varlen" in paths:
         q = st["varlen"][0]
         dev_out["varlen"] = (torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda"))
@@ -184,6 +198,10 @@ def run_gpu(paths, steps, warmup):
             q, k, v = st["decode"]
             o, lse, ws = dev_out["decode"]
             am.attn_decode_splitkv(q, k, v, workspace=ws, out=o, lse=lse)
+        elif name == "decode_fp8":
+            q, k8, v8, ks, vs = st["decode_fp8"]
+            o, lse, ws = dev_out["decode_fp8"]
+            am.attn_decode_splitkv_fp8(q, k8, v8, ks, vs, workspace=ws, out=o, lse=lse)
         elif name == "varlen":
             q, k, v, cq, ck, mq = st["varlen"]
             o, lse = dev_out["varlen"]
@@ -193,7 +211,7 @@ def run_gpu(paths, steps, warmup):
             o, lse, dq, dk, dv, ws = dev_out["bwd"]
             am.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
 
-    order = [p for p in ("fwd", "decode", "bwd", "varlen") if p in paths]
+    order = [p for p in ("fwd", "decode", "bwd", "decode_fp8", "varlen") if p in paths]
     for _ in range(warmup):
         for p in order:
             run_path(p)
@@ -348,6 +366,14 @@ def main():
                                  "tflops": round(f / t / 1e9, 2), "frac_mfma": round(f / t / 1e9 / PEAK_BF16_TFLOPS, 4),
                                  "shape": "B=4 H=16 N=2048 d=128 causal"}
         total_flops += f
+    if "decode_fp8" in paths:
+        c = DECODE
+        b = decode_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], kv_bytes_per_elem=1)
+        t = sum(per["decode_fp8"]) / len(per["decode_fp8"])
+        out_paths["decode_fp8"] = {"ms": round(t, 4), "ms_median": round(med(per["decode_fp8"]), 4),
+                                   "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
+                                   "shape": "48 streams, Hq=32 Hkv=8 d=128, 4096 keys, FP8 E4M3 KV cache"}
+        total_flops += decode_flops(c["B"], c["Hq"], c["L"], c["d"])
     if "varlen" in paths:
         c = VARLEN
         lens_q, lens_k = st["varlen_lens"]

@@ -115,6 +115,24 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 void* stream);
 
 /*
+ * Split-KV decode over an FP8 KV cache: k and v hold OCP FP8 E4M3 codes
+ * (1 byte per element, [B,Hkv,Nk,d]; 0x7F / 0xFF are NaN and propagate), and
+ * kv head h's values are k_scale[h] * code and v_scale[h] * code (k_scale,
+ * v_scale: device fp32 arrays of Hkv scales shared by the batch).  q and o
+ * are bf16 [B,Hq,1,d]; lse fp32 [B,Hq] (may be NULL).  The codes are widened
+ * to bf16 exactly on the GPU and the scales enter in fp32, so the result is
+ * attn_decode_splitkv's on the dequantized cache; only the KV traffic halves.
+ * Workspace as attn_decode_workspace_bytes; every other rule as
+ * attn_decode_splitkv.  FP8 KV caches are what the second page's fastest
+ * compared engine serves ("Tang Project Derives GPU Kernels via IR ...",
+ * section "Details").
+ */
+attn_status attn_decode_splitkv_fp8(const void* q, const void* k, const void* v, const float* k_scale,
+                                    const float* v_scale, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                                    int64_t Nq, int64_t Nk, int64_t d, float scale, int num_splits, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Backward from the saved log-sum-exp.  Inputs q, k, v, o, dout (dtype) and
  * lse (fp32, as written by attn_fwd with the same arguments); outputs dq
  * [B,Hq,Nq,d], dk and dv [B,Hkv,Nk,d], all fp32 and fully overwritten (dk and

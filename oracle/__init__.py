@@ -175,6 +175,41 @@ def fwd_varlen_rows(q, k, v, cu_q, cu_k, rows, scale: float, causal: bool):
     return o, lse
 
 
+def e4m3_value(codes) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> fp64 values, from the format's
+    definition: bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa;
+    exponent 0 encodes (m / 8) 2^-6, otherwise (1 + m / 8) 2^(e - 7); the
+    all-ones exponent and mantissa (0x7F, 0xFF) is NaN; no infinities."""
+    c = np.asarray(codes, np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def decode_fp8(q, k8, v8, k_scale, v_scale, scale: float):
+    """One decode query per stream against an FP8 cache: the keys and values
+    are k_scale[h] * E4M3(code) and v_scale[h] * E4M3(code) for kv head h,
+    every key visible.  Solved per kv head with fwd above on the exact code
+    values (fp32-exact) and the scales applied in fp64: the scores take
+    scale * k_scale[h] as their scale and O is multiplied by v_scale[h] (the
+    softmax weights do not depend on v).  Returns (O [B,Hq,1,d], LSE [B,Hq,1])."""
+    q = _f32(q)
+    B, Hq, Nq, d = q.shape
+    Hkv = np.asarray(k8).shape[1]
+    g = Hq // Hkv
+    o = np.empty((B, Hq, Nq, d))
+    lse = np.empty((B, Hq, Nq))
+    for h in range(Hkv):
+        k = e4m3_value(np.asarray(k8)[:, h:h + 1]).astype(np.float32)
+        v = e4m3_value(np.asarray(v8)[:, h:h + 1]).astype(np.float32)
+        oh, lh = fwd(q[:, h * g:(h + 1) * g], k, v, float(scale) * float(k_scale[h]), False)
+        o[:, h * g:(h + 1) * g] = oh * float(v_scale[h])
+        lse[:, h * g:(h + 1) * g] = lh
+    return o, lse
+
+
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel regions use."""
     return int(lib().oracle_num_threads())

@@ -111,3 +111,35 @@ def chunked_prefill_lengths(seed: int, n: int, lq_range, history_range):
     lq = rng.integers(lq_range[0], lq_range[1] + 1, size=n)
     h = rng.integers(history_range[0], history_range[1] + 1, size=n)
     return [int(x) for x in lq], [int(x + y) for x, y in zip(h, lq)]
+
+
+def quantize_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
+    """x / scale to the nearest OCP FP8 E4M3 code (ties to the even code),
+    saturating at +-448; uint8 codes of x's shape.  Test-input encoding only.
+    E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+    holds the subnormals m 2^-9.  Normal values round the fp32 significand to
+    3 bits (round to nearest even on the bits dropped) and rebias the
+    exponent; values below 2^-6 round to the nearest multiple of 2^-9."""
+    x = np.asarray(x, np.float32)
+    y = np.minimum(np.abs(x) * np.float32(1.0 / float(scale)), np.float32(448.0))
+    bits = y.view(np.int32)
+    r = (bits + 0x7FFFF + ((bits >> 20) & 1)) >> 20      # exponent and 3 rounded mantissa bits
+    code = r - (120 << 3)                                  # fp32 bias 127 -> E4M3 bias 7
+    small = y < np.float32(2.0 ** -6)
+    code[small] = np.rint(y[small] * np.float32(512.0)).astype(np.int32)
+    np.minimum(code, 0x7E, out=code)
+    code[(x < 0) & (code > 0)] |= 0x80
+    return code.astype(np.uint8)
+
+
+def fp8_kv_inputs(seed: int, B: int, Hq: int, Hkv: int, Nk: int, d: int):
+    """Decode inputs with an FP8 cache: q bf16-exact [B,Hq,1,d] (fp32 array),
+    K, V codes uint8 [B,Hkv,Nk,d] and per-kv-head scales (max |x| / 448 over the
+    head, as an fp32 value), drawn as attn_inputs(seed, ...) draws them."""
+    q, k, v = attn_inputs(seed, B, Hq, Hkv, 1, Nk, d, bf16=False)
+    q = bf16_bits_to_f32(round_bf16_bits(q)).reshape(q.shape)
+    ks = np.array([max(float(np.abs(k[:, h]).max()), 1e-30) / 448.0 for h in range(Hkv)], np.float32)
+    vs = np.array([max(float(np.abs(v[:, h]).max()), 1e-30) / 448.0 for h in range(Hkv)], np.float32)
+    k8 = np.stack([quantize_e4m3(k[:, h], ks[h]) for h in range(Hkv)], axis=1)
+    v8 = np.stack([quantize_e4m3(v[:, h], vs[h]) for h in range(Hkv)], axis=1)
+    return q, k8, v8, ks, vs

@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_fwd_varlen", "attn_decode_splitkv", "attn_bwd", "attn_decode_workspace_bytes",
+    for n in ("attn_fwd", "attn_fwd_varlen", "attn_decode_splitkv", "attn_decode_splitkv_fp8", "attn_bwd",
+              "attn_decode_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_decode_num_splits", "attn_strerror"):
         assert n in names
 
@@ -151,6 +152,40 @@ def dec(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scal
 )
 def test_decode_rejects(kw, code):
     assert dec(**kw) == code
+
+
+def dec8(q=P, k=P, v=P, ks=P, vs=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scale=0.088, splits=0,
+         ws=P, ws_bytes=1 << 30):
+    return am.lib().attn_decode_splitkv_fp8(q, k, v, ks, vs, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, splits, ws,
+                                            ws_bytes, None)
+
+
+@no_gpu
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(Nq=2), am.ATTN_ERR_INVALID),
+        (dict(splits=-1), am.ATTN_ERR_INVALID),
+        (dict(q=NUL), am.ATTN_ERR_INVALID),
+        (dict(k=NUL), am.ATTN_ERR_INVALID),
+        (dict(ks=NUL), am.ATTN_ERR_INVALID),
+        (dict(vs=NUL), am.ATTN_ERR_INVALID),
+        (dict(scale=0.0), am.ATTN_ERR_INVALID),
+        (dict(Hq=30), am.ATTN_ERR_INVALID),
+        (dict(Hq=64, Hkv=1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(ws=NUL), am.ATTN_ERR_WORKSPACE),
+        (dict(ws_bytes=16), am.ATTN_ERR_WORKSPACE),
+        (dict(d=80), am.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_decode_fp8_rejects(kw, code):
+    assert dec8(**kw) == code
+
+
+@no_gpu
+def test_decode_fp8_empty_launches_nothing():
+    assert dec8(q=NUL, k=NUL, v=NUL, ks=NUL, vs=NUL, o=NUL, lse=NUL, B=0) == am.ATTN_OK
+    assert dec8(q=NUL, k=NUL, v=NUL, ks=NUL, vs=NUL, o=NUL, lse=NUL, Nq=0) == am.ATTN_OK
 
 
 def test_split_plan_and_workspace():
