@@ -32,6 +32,12 @@ constexpr float kTau = 8.0f;
 #define ATTN_DECODE_WAVES 4
 #endif
 constexpr int kWaves = ATTN_DECODE_WAVES;
+// LDS stages per wave of the FP8 kernel.  Two stages (64 KB of tiles, so two
+// workgroups share a CU) measured faster than three or four (one workgroup
+// per CU, more tiles in flight per wave) at 48 x 4096, 16 x 4096 and 48 x 2048.
+#ifndef ATTN_DECODE_FP8_STAGES
+#define ATTN_DECODE_FP8_STAGES 2
+#endif
 
 struct DecArgs {
   const __bf16* q;
@@ -233,8 +239,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
 // ---------------------------------------------------------------------------
 // Split-KV decode over an FP8 (OCP E4M3) KV cache with a scale per kv head.
 // Same decomposition and fold as the bf16 kernel; K and V move HBM -> LDS as
-// bytes (half the traffic), four stages per wave (three tiles in flight, the
-// same LDS as the bf16 kernel's two), and are widened to bf16 in registers
+// bytes (half the traffic) through a ring of LDS stages per wave, and are
+// widened to bf16 in registers
 // just before the MFMAs, which is exact.  The K scale folds into the exponent
 // scale and the V scale into the accumulator, so the arithmetic after the
 // loads is the bf16 kernel's.
@@ -249,15 +255,16 @@ template <int D>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_fp8_kernel(DecArgs a) {
   constexpr int BN = kDecodeTile;
   constexpr int TILE = BN * D;           // bytes of one K or V tile
-  constexpr int NST = 4;                 // stages per wave
+  constexpr int NST = ATTN_DECODE_FP8_STAGES;  // stages per wave
   constexpr int STAGE = 2 * TILE;        // K then V
   constexpr int CPR = D / 16;            // 16-byte chunks per row
   constexpr int LOADS = BN * CPR / 64;   // per lane per K (or V) tile
   constexpr int VMT = 2 * LOADS;         // loads per wave per tile
   static_assert(BN == 32, "one 32-key MFMA block per tile");
   static_assert(LOADS * 64 == BN * CPR, "tile must split evenly over a wave");
-  static_assert(kWaves * NST * STAGE >= kWaves * 32 * D * 4 + 2 * kWaves * 32 * 4, "fold area fits the tiles");
-  __shared__ __attribute__((aligned(1024))) char smem[kWaves * NST * STAGE];
+  constexpr int FOLD = kWaves * 32 * D * 4 + 2 * kWaves * 32 * 4;  // the fold's area, reusing the tiles'
+  constexpr int SMEM = kWaves * NST * STAGE > FOLD ? kWaves * NST * STAGE : FOLD;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
