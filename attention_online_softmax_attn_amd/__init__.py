@@ -8,6 +8,7 @@ not built, or a tensor is not on the GPU, these functions raise.
     attn_fwd(q, k, v, causal, scale)                  -> (o, lse)
     attn_fwd_varlen(q, k, v, cu_q, cu_k, max_q, ...)  -> (o, lse)
     attn_decode_splitkv(q, k, v, scale, num_splits=0) -> (o, lse)
+    attn_decode_splitkv_fused(q, k, v, scale, num_splits=0)  -> (o, lse)
     attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, ...) -> (o, lse)
     attn_bwd(q, k, v, o, dout, lse, causal, scale)    -> (dq, dk, dv)
 
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci, vp, sz, ci, vp]
     L.attn_decode_splitkv.restype = ci
+    L.attn_decode_fused_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
+    L.attn_decode_fused_workspace_bytes.restype = sz
+    L.attn_decode_splitkv_fused.argtypes = L.attn_decode_splitkv.argtypes
+    L.attn_decode_splitkv_fused.restype = ci
     L.attn_decode_splitkv_fp8.argtypes = [vp] * 7 + [i64] * 6 + [f32, ci, vp, sz, vp]
     L.attn_decode_splitkv_fp8.restype = ci
     L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
@@ -188,6 +193,33 @@ def attn_decode_splitkv(q, k, v, scale=None, num_splits: int = 0, workspace=None
                                    _dtype_code(q), _stream())
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_splitkv")
+    return o, (lse if want_lse else None)
+
+
+def decode_fused_workspace_bytes(B: int, Hq: int, Hkv: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    return int(lib().attn_decode_fused_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits))
+
+
+def attn_decode_splitkv_fused(q, k, v, scale=None, num_splits: int = 0, workspace=None, out=None, lse=None,
+                              want_lse: bool = True):
+    """Split-KV decode in one launch (the last split to finish merges).  A
+    workspace passed in must have been zeroed before its first use (its
+    arrival counts are left zero by every call); without one a zeroed one is
+    allocated.  Returns (o, lse)."""
+    _check_dev(q, k, v, out, lse, workspace)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = decode_fused_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_splitkv_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if want_lse else None, B, Hq,
+                                         Hkv, Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _ptr(workspace),
+                                         ws_bytes, _dtype_code(q), _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_splitkv_fused")
     return o, (lse if want_lse else None)
 
 

@@ -69,6 +69,12 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int requested) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The single-launch decode's arrival counts: a fixed region at the start of
+// its workspace, one 4-byte count per (stream, kv head), so that no call's
+// partial states ever overlap a count another call may use.
+constexpr size_t kDecodeCountBytes = 65536;
+constexpr int64_t kDecodeMaxPairs = (int64_t)(kDecodeCountBytes / sizeof(unsigned));
+
 }  // namespace
 
 extern "C" {
@@ -132,12 +138,18 @@ size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N
   return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
+size_t attn_decode_fused_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
+  const size_t parts = attn_decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits);
+  if (parts == 0) return 0;
+  return kDecodeCountBytes + parts;
+}
+
 }  // extern "C"
 
 namespace {
 
 attn_status decode_common(const void* q, const void* k, const void* v, const float* k_scale, const float* v_scale,
-                          bool fp8, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                          bool fp8, bool fused, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                           int64_t d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
                           attn_dtype dtype, void* stream) {
   attn_status st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
@@ -165,11 +177,20 @@ attn_status decode_common(const void* q, const void* k, const void* v, const flo
   p.num_splits = sp.splits;
   p.chunk = sp.chunk;
   if (sp.splits > 1) {
-    const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits);
+    const size_t need = fused ? attn_decode_fused_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
+                              : attn_decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits);
     if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    // the arrival counts take device atomics: 4-byte alignment
+    if (fused && ((uintptr_t)workspace & 3) != 0) return ATTN_ERR_INVALID;
+    char* ws = (char*)workspace;
+    if (fused) {
+      if (B * Hkv > kDecodeMaxPairs) return ATTN_ERR_UNSUPPORTED;
+      p.counters = (unsigned*)ws;
+      ws += kDecodeCountBytes;
+    }
     const size_t rows = (size_t)B * Hq * sp.splits;
-    p.part_acc = (float*)workspace;
-    p.part_ml = (float*)((char*)workspace + align256(rows * d * sizeof(float)));
+    p.part_acc = (float*)ws;
+    p.part_ml = (float*)(ws + align256(rows * d * sizeof(float)));
   }
   if (fp8 && Nk > 0) {
     p.k8 = (const uint8_t*)k;
@@ -189,15 +210,24 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 int num_splits, void* workspace, size_t workspace_bytes, attn_dtype dtype,
                                 void* stream) {
   (void)causal;  // one bottom-right-aligned query sees every key
-  return decode_common(q, k, v, nullptr, nullptr, false, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits, workspace,
+  return decode_common(q, k, v, nullptr, nullptr, false, false, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits, workspace,
                        workspace_bytes, dtype, stream);
+}
+
+attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                      int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                      int causal, int num_splits, void* workspace, size_t workspace_bytes,
+                                      attn_dtype dtype, void* stream) {
+  (void)causal;
+  return decode_common(q, k, v, nullptr, nullptr, false, true, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits,
+                       workspace, workspace_bytes, dtype, stream);
 }
 
 attn_status attn_decode_splitkv_fp8(const void* q, const void* k, const void* v, const float* k_scale,
                                     const float* v_scale, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
                                     int64_t Nq, int64_t Nk, int64_t d, float scale, int num_splits, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  return decode_common(q, k, v, k_scale, v_scale, true, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits, workspace,
+  return decode_common(q, k, v, k_scale, v_scale, true, false, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits, workspace,
                        workspace_bytes, ATTN_BF16, stream);
 }
 

@@ -56,7 +56,66 @@ struct DecArgs {
   const uint8_t* v8;
   const float* k_scale;
   const float* v_scale;
+  // single-launch mode (null: a merge kernel folds the splits): one arrival
+  // count per (stream, kv head), zero on entry and left zero on exit
+  unsigned* counters;
 };
+
+// The partial states are written and, in single-launch mode, read back by
+// workgroups on other XCDs, whose L2 caches are not coherent with each
+// other.  Device-scope relaxed accesses keep them coherent per access (the
+// store writes through to memory, the load fetches from it) instead of a
+// device-scope fence, which writes back or invalidates a whole L2 (measured:
+// the fences doubled the 48 x 4096 decode).
+__device__ __forceinline__ void store_agent(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Fold the num_splits partial states of row (b, query head) for output
+// column col and write O (and LSE from column 0).  The merge kernel and the
+// single-launch path share it, so both give the same bits.
+template <int D>
+__device__ __forceinline__ void fold_split_states(const DecArgs& a, size_t row, int col) {
+  const float* ml = a.part_ml + row * a.S * 2;
+  float M = kNegInf;
+  for (int s = 0; s < a.S; s++) M = fmaxf(M, load_agent(ml + 2 * s));
+  float L = 0.0f, A = 0.0f;
+  for (int s = 0; s < a.S; s++) {
+    const float ms = load_agent(ml + 2 * s);
+    const float f = (ms == kNegInf) ? 0.0f : fast_exp2(ms - M);
+    L += f * load_agent(ml + 2 * s + 1);
+    A += f * load_agent(a.part_acc + (row * a.S + s) * D + col);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  a.o[row * D + col] = to_bf16(A * inv);
+  if (col == 0 && a.lse != nullptr) a.lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+}
+
+// Single-launch split-KV: called by every thread of a workgroup once it has
+// issued its partial state's (write-through) stores.  Each thread waits for
+// its stores to complete, then the workgroup counts itself in for its
+// (stream, kv head) with a device-scope atomic; the workgroup that arrives
+// last (every other split's stores completed before that split counted in)
+// folds all splits of its g query rows, reading them from memory, and returns
+// the count to zero for the next call.
+template <int D>
+__device__ void merge_if_last(const DecArgs& a, int b, int kvh, int pair) {
+  __shared__ unsigned s_last;
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(a.counters + pair, 1u) == (unsigned)(a.S - 1) ? 1u : 0u;
+  __syncthreads();
+  if (s_last == 0u) return;
+  const int total = a.g * D;
+  for (int e = threadIdx.x; e < total; e += kWaves * 64) {
+    const int qh = e / D, col = e % D;
+    fold_split_states<D>(a, (size_t)b * a.Hq + kvh * a.g + qh, col);
+  }
+  if (threadIdx.x == 0) atomicExch(a.counters + pair, 0u);
+}
 
 template <int D>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs a) {
@@ -227,13 +286,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
       a.o[row * D + col] = to_bf16(L > 0.0f ? A / L : 0.0f);
       if (col == 0 && a.lse != nullptr) a.lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
     } else {
-      a.part_acc[(row * a.S + split) * D + col] = A;
+      store_agent(a.part_acc + (row * a.S + split) * D + col, A);
       if (col == 0) {
-        a.part_ml[(row * a.S + split) * 2 + 0] = M;
-        a.part_ml[(row * a.S + split) * 2 + 1] = L;
+        store_agent(a.part_ml + (row * a.S + split) * 2 + 0, M);
+        store_agent(a.part_ml + (row * a.S + split) * 2 + 1, L);
       }
     }
   }
+  if (a.S > 1 && a.counters != nullptr) merge_if_last<D>(a, b, kvh, pair);
 }
 
 // ---------------------------------------------------------------------------
@@ -434,13 +494,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_fp8_kernel(DecA
       a.o[row * D + col] = to_bf16(L > 0.0f ? A / L : 0.0f);
       if (col == 0 && a.lse != nullptr) a.lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
     } else {
-      a.part_acc[(row * a.S + split) * D + col] = A;
+      store_agent(a.part_acc + (row * a.S + split) * D + col, A);
       if (col == 0) {
-        a.part_ml[(row * a.S + split) * 2 + 0] = M;
-        a.part_ml[(row * a.S + split) * 2 + 1] = L;
+        store_agent(a.part_ml + (row * a.S + split) * 2 + 0, M);
+        store_agent(a.part_ml + (row * a.S + split) * 2 + 1, L);
       }
     }
   }
+  if (a.S > 1 && a.counters != nullptr) merge_if_last<D>(a, b, kvh, pair);
 }
 
 // Fold num_splits partial states per (b, query head).  One wave per row.
@@ -449,25 +510,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= a.B * a.Hq) return;
-  const float* ml = a.part_ml + (size_t)row * a.S * 2;
-  float M = kNegInf;
-  for (int s = 0; s < a.S; s++) M = fmaxf(M, ml[2 * s]);
-  float L = 0.0f;
-  float A[D / 64];
 #pragma unroll
-  for (int e = 0; e < D / 64; e++) A[e] = 0.0f;
-  for (int s = 0; s < a.S; s++) {
-    const float ms = ml[2 * s];
-    const float f = (ms == kNegInf) ? 0.0f : fast_exp2(ms - M);
-    L += f * ml[2 * s + 1];
-    const float* pa = a.part_acc + ((size_t)row * a.S + s) * D;
-#pragma unroll
-    for (int e = 0; e < D / 64; e++) A[e] += f * pa[e * 64 + lane];
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-  for (int e = 0; e < D / 64; e++) a.o[(size_t)row * D + e * 64 + lane] = to_bf16(A[e] * inv);
-  if (lane == 0 && a.lse != nullptr) a.lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+  for (int e = 0; e < D / 64; e++) fold_split_states<D>(a, (size_t)row, e * 64 + lane);
 }
 
 template <int D>
@@ -493,12 +537,13 @@ hipError_t launch(const DecodeProblem& p, hipStream_t s) {
   a.v8 = p.v8;
   a.k_scale = p.k_scale;
   a.v_scale = p.v_scale;
+  a.counters = p.counters;
   if (p.k8 != nullptr)
     hipLaunchKernelGGL((decode_partial_fp8_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
   else
     hipLaunchKernelGGL((decode_partial_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.S == 1) return e;
+  if (e != hipSuccess || a.S == 1 || a.counters != nullptr) return e;
   const int rows = a.B * a.Hq;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -47,6 +47,10 @@ struct DecodeProblem {
   const uint8_t* v8 = nullptr;
   const float* k_scale = nullptr;
   const float* v_scale = nullptr;
+  // single launch (null: a second kernel merges the splits): [B * Hkv]
+  // arrival counts, zero on entry; the last split of each (stream, kv head)
+  // to finish merges them and returns its count to zero
+  unsigned* counters = nullptr;
 };
 // Keys per decode tile; split chunks are whole multiples of it.
 constexpr int kDecodeTile = 32;

@@ -19,9 +19,11 @@ cpu_baseline = the CPU oracle on a bounded sample of the same step's work
 
 Opt-in paths (not part of the default step): varlen = chunked prefill of a
 packed batch of 16 sequences (attn_fwd_varlen); decode_fp8 = the decode shape
-over an FP8 E4M3 KV cache (attn_decode_splitkv_fp8).
+over an FP8 E4M3 KV cache (attn_decode_splitkv_fp8); decode_fused = the decode
+shape in one launch (attn_decode_splitkv_fused, the last split merges).
 
-Usage: python bench.py [--steps K] [--warmup W] [--no-cpu] [--paths fwd,decode,bwd[,varlen][,decode_fp8]]
+Usage: python bench.py [--steps K] [--warmup W] [--no-cpu]
+                       [--paths fwd,decode,bwd[,varlen][,decode_fp8][,decode_fused]]
 """
 from __future__ import annotations
 
@@ -128,6 +130,10 @@ def setup(paths):
         q, k, v = synth.attn_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], 1, c["L"], c["d"], bf16=True)
         st["decode_host"] = (q, k, v)
         st["decode"] = (to_dev(q), to_dev(k), to_dev(v))
+    if "decode_fused" in paths:
+        c = DECODE
+        q, k, v = synth.attn_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], 1, c["L"], c["d"], bf16=True)
+        st["decode_fused"] = (to_dev(q), to_dev(k), to_dev(v))
     if "bwd" in paths:
         c = BACKWARD
         q, k, v, do = synth.attn_inputs(c["seed"], c["B"], c["H"], c["H"], c["N"], c["N"], c["d"], bf16=True,
@@ -184,6 +190,13 @@ def run_gpu(paths, steps, warmup):
         ws = am.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], 0)
         dev_out["decode_fp8"] = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"),
                                  torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda"))
+    if "decode_fused" in paths:
+        q = st["decode_fused"][0]
+        c = DECODE
+        ws = am.decode_fused_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], 0)
+        # the arrival counts start at zero; every call leaves them zero
+        dev_out["decode_fused"] = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"),
+                                   torch.zeros(max(ws, 1), dtype=torch.uint8, device="cuda"))
     if "varlen" in paths:
         q = st["varlen"][0]
         dev_out["varlen"] = (torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda"))
@@ -202,6 +215,10 @@ def run_gpu(paths, steps, warmup):
             q, k8, v8, ks, vs = st["decode_fp8"]
             o, lse, ws = dev_out["decode_fp8"]
             am.attn_decode_splitkv_fp8(q, k8, v8, ks, vs, workspace=ws, out=o, lse=lse)
+        elif name == "decode_fused":
+            q, k, v = st["decode_fused"]
+            o, lse, ws = dev_out["decode_fused"]
+            am.attn_decode_splitkv_fused(q, k, v, workspace=ws, out=o, lse=lse)
         elif name == "varlen":
             q, k, v, cq, ck, mq = st["varlen"]
             o, lse = dev_out["varlen"]
@@ -211,7 +228,7 @@ def run_gpu(paths, steps, warmup):
             o, lse, dq, dk, dv, ws = dev_out["bwd"]
             am.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
 
-    order = [p for p in ("fwd", "decode", "bwd", "decode_fp8", "varlen") if p in paths]
+    order = [p for p in ("fwd", "decode", "bwd", "decode_fp8", "decode_fused", "varlen") if p in paths]
     for _ in range(warmup):
         for p in order:
             run_path(p)
@@ -373,6 +390,14 @@ def main():
         out_paths["decode_fp8"] = {"ms": round(t, 4), "ms_median": round(med(per["decode_fp8"]), 4),
                                    "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
                                    "shape": "48 streams, Hq=32 Hkv=8 d=128, 4096 keys, FP8 E4M3 KV cache"}
+        total_flops += decode_flops(c["B"], c["Hq"], c["L"], c["d"])
+    if "decode_fused" in paths:
+        c = DECODE
+        b = decode_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"])
+        t = sum(per["decode_fused"]) / len(per["decode_fused"])
+        out_paths["decode_fused"] = {"ms": round(t, 4), "ms_median": round(med(per["decode_fused"]), 4),
+                                     "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
+                                     "shape": "48 streams, Hq=32 Hkv=8 d=128, 4096 keys, one launch"}
         total_flops += decode_flops(c["B"], c["Hq"], c["L"], c["d"])
     if "varlen" in paths:
         c = VARLEN

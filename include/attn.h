@@ -115,6 +115,36 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 void* stream);
 
 /*
+ * Split-KV decode in one launch.  Same arguments, rules and result as
+ * attn_decode_splitkv (the same kernels and the same fold, so the same bits),
+ * but no merge kernel: each chunk's workgroup publishes its partial state
+ * and counts itself in for its (stream, kv head) with a device atomic, and
+ * the last one to arrive folds every chunk's state and writes o and lse.
+ * It folds the chunks in index order whichever finishes last, so the result
+ * does not depend on timing.  The fold is the online-softmax monoid of "Não
+ * escreva kernels, derive-os" (section "Aprofundamento"); "Tang Project
+ * Derives GPU Kernels via IR ..." (section "Details") ties decode accuracy to
+ * the split granularity.
+ *   Workspace attn_decode_fused_workspace_bytes bytes (0 when the plan has
+ *             one chunk: then no workspace is read), 4-byte aligned
+ *             (ATTN_ERR_INVALID otherwise).  Its first 64 KiB hold the
+ *             arrival counts, one per (stream, kv head), so B * Hkv <= 16384
+ *             when the plan has more than one chunk (ATTN_ERR_UNSUPPORTED
+ *             otherwise); the partial states follow.  The counts must be zero
+ *             before the first call on that memory (allocate it zeroed);
+ *             every call that completes leaves them zero, so the workspace
+ *             serves later calls of any size that fits.  Calls that share a
+ *             workspace must not run concurrently (stream order suffices),
+ *             and memory used by another entry point must be zeroed again
+ *             before it serves this one.
+ */
+size_t attn_decode_fused_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits);
+attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                      int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                      int causal, int num_splits, void* workspace, size_t workspace_bytes,
+                                      attn_dtype dtype, void* stream);
+
+/*
  * Split-KV decode over an FP8 KV cache: k and v hold OCP FP8 E4M3 codes
  * (1 byte per element, [B,Hkv,Nk,d]; 0x7F / 0xFF are NaN and propagate), and
  * kv head h's values are k_scale[h] * code and v_scale[h] * code (k_scale,

@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_varlen", "attn_decode_splitkv", "attn_decode_splitkv_fp8", "attn_bwd",
-              "attn_decode_workspace_bytes",
+              "attn_decode_splitkv_fused", "attn_decode_fused_workspace_bytes", "attn_decode_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_decode_num_splits", "attn_strerror"):
         assert n in names
 
@@ -152,6 +152,49 @@ def dec(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scal
 )
 def test_decode_rejects(kw, code):
     assert dec(**kw) == code
+
+
+def decf(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scale=0.088, splits=0, ws=P,
+         ws_bytes=1 << 30, dt=am.ATTN_BF16):
+    return am.lib().attn_decode_splitkv_fused(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, 0, splits, ws, ws_bytes,
+                                              dt, None)
+
+
+@no_gpu
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(Nq=2), am.ATTN_ERR_INVALID),
+        (dict(splits=-1), am.ATTN_ERR_INVALID),
+        (dict(q=NUL), am.ATTN_ERR_INVALID),
+        (dict(dt=am.ATTN_F32), am.ATTN_ERR_UNSUPPORTED),
+        (dict(ws=NUL), am.ATTN_ERR_WORKSPACE),
+        (dict(ws=ctypes.c_void_p(0x100002)), am.ATTN_ERR_INVALID),   # counts need 4-byte alignment
+        (dict(d=80), am.ATTN_ERR_UNSUPPORTED),
+        (dict(B=4097, Nk=512, splits=2), am.ATTN_ERR_UNSUPPORTED),      # more pairs than counts
+    ],
+)
+def test_decode_fused_rejects(kw, code):
+    assert decf(**kw) == code
+
+
+@no_gpu
+def test_decode_fused_workspace_must_hold_the_counts():
+    # exactly the two-launch workspace is too small: the counts come first
+    B, Hq, Hkv, L, d = 2, 32, 8, 4096, 128
+    need2 = am.decode_workspace_bytes(B, Hq, Hkv, L, d, 0)
+    assert decf(ws_bytes=need2) == am.ATTN_ERR_WORKSPACE
+    assert decf(ws_bytes=am.decode_fused_workspace_bytes(B, Hq, Hkv, L, d, 0) - 1) == am.ATTN_ERR_WORKSPACE
+
+
+def test_decode_fused_workspace_layout():
+    for B, L, s in [(1, 512, 0), (48, 4096, 0), (16, 4096, 3), (2, 4096, 1), (48, 4096, 128)]:
+        two = am.decode_workspace_bytes(B, 32, 8, L, 128, s)
+        one = am.decode_fused_workspace_bytes(B, 32, 8, L, 128, s)
+        if two == 0:
+            assert one == 0                       # one chunk: no partials, no counts
+        else:
+            assert one == two + 65536                # a fixed region of arrival counts first
 
 
 def dec8(q=P, k=P, v=P, ks=P, vs=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scale=0.088, splits=0,
