@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci, vp, sz, ci, vp]
     L.attn_decode_splitkv.restype = ci
+    L.attn_decode_fused_num_splits.argtypes = [i64, i64, i64, i64, i64]
+    L.attn_decode_fused_num_splits.restype = ci
     L.attn_decode_fused_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
     L.attn_decode_fused_workspace_bytes.restype = sz
     L.attn_decode_splitkv_fused.argtypes = L.attn_decode_splitkv.argtypes
@@ -194,6 +196,10 @@ def attn_decode_splitkv(q, k, v, scale=None, num_splits: int = 0, workspace=None
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_splitkv")
     return o, (lse if want_lse else None)
+
+
+def decode_fused_num_splits(B: int, Hq: int, Hkv: int, Nk: int, d: int) -> int:
+    return int(lib().attn_decode_fused_num_splits(B, Hq, Hkv, Nk, d))
 
 
 def decode_fused_workspace_bytes(B: int, Hq: int, Hkv: int, Nk: int, d: int, num_splits: int = 0) -> int:

@@ -2,6 +2,7 @@
 // HIP call), the split-KV plan, workspace layout and kernel dispatch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -10,7 +11,7 @@
 
 namespace {
 
-constexpr int kNumCUs = 256;  // MI355X compute units; the split plan targets whole waves of workgroups
+constexpr int kNumCUs = 256;  // MI355X compute units (the decode split plan counts waves of workgroups)
 
 bool dims_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk) {
   return B >= 0 && Hq >= 1 && Hkv >= 1 && Nq >= 0 && Nk >= 0 && Hq % Hkv == 0;
@@ -36,29 +37,43 @@ struct SplitPlan {
   int chunk;
 };
 
-// Choose the number of key chunks per (b, kv head): the smallest count whose
-// total workgroup count fills the GPU's workgroup slots in the most nearly
-// whole waves, keeping at least 4 key tiles per chunk.
-SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int requested) {
+// Choose the number of key chunks per (b, kv head) from a cost model of the
+// decode, with constants measured on MI355X at d = 128:
+//   - one workgroup streams its chunk at ~121 keys/us (bf16 cache; ~92 for
+//     the FP8 kernel, which widens the codes in registers) after ~2 us of
+//     start-up, and the workgroups of a launch run in waves of one per CU
+//     (two for the FP8 kernel, whose tiles take half the LDS);
+//   - the whole decode reads at most ~5.6 TB/s;
+//   - each extra chunk costs ~0.2 us in the fold, and the two-launch path a
+//     further ~2.5 us for the merge launch.
+// Candidates are 1, 2, 4, ... chunks of at least one key tile, at most 64;
+// a larger count must beat the smaller by 5 % (the model's resolution).
+// Splitting pays only where too few workgroups would stream the cache: from
+// 16 streams x 8 kv heads up a bf16 cache takes one chunk per (b, kv head).
+SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int requested, bool fused, bool fp8) {
   const int tile = attn::kDecodeTile;
   const int64_t tiles = Nk > 0 ? (Nk + tile - 1) / tile : 1;
   int s;
   if (requested > 0) {
     s = requested;
   } else {
-    const int64_t units = B * Hkv;
-    const int64_t s_max = std::max<int64_t>(1, tiles / 4);
-    double best = -1.0;
+    constexpr double kHbmBytesPerUs = 5.6e6, kWgStartUs = 2.0, kFoldUsPerSplit = 0.2, kMergeLaunchUs = 2.5;
+    const double keys_per_us = fp8 ? 92.0 : 121.0;
+    const double slots = kNumCUs * (fp8 ? 2.0 : 1.0);
+    const double units = (double)(B * Hkv);
+    const double key_bytes = 2.0 * (double)d * (fp8 ? 1.0 : 2.0);  // K and V
+    const double hbm_us = units * (double)Nk * key_bytes / kHbmBytesPerUs;
+    double best = 0.0;
     s = 1;
-    for (int64_t c = 1; c <= std::min<int64_t>(s_max, 64); c++) {
-      const int64_t wgs = units * c;
-      const double waves = (double)wgs / kNumCUs;
-      const double eff = waves / std::ceil(waves);
-      if (eff > best + 1e-9) {
-        best = eff;
+    for (int64_t c = 1; c <= std::min<int64_t>(tiles, 64); c *= 2) {
+      const double chunk_keys = (double)(((tiles + c - 1) / c) * tile);
+      const double waves = std::ceil(units * (double)c / slots);
+      double t = std::max(waves * (kWgStartUs + chunk_keys / keys_per_us), hbm_us);
+      if (c > 1) t += kFoldUsPerSplit * (double)c + (fused ? 0.0 : kMergeLaunchUs);
+      if (c == 1 || t < 0.95 * best) {
+        best = t;
         s = (int)c;
       }
-      if (wgs >= 4 * kNumCUs) break;
     }
   }
   if (s > tiles) s = (int)tiles;
@@ -127,19 +142,39 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
 
 int attn_decode_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d) {
   if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128)) return -1;
-  return plan_splits(B, Hkv, Nk, 0).splits;
+  return plan_splits(B, Hkv, Nk, d, 0, false, false).splits;
 }
 
-size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
-  if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128) || num_splits < 0) return 0;
-  SplitPlan sp = plan_splits(B, Hkv, Nk, num_splits);
+int attn_decode_fused_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d) {
+  if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128)) return -1;
+  return plan_splits(B, Hkv, Nk, d, 0, true, false).splits;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Bytes of the partial states (m, l, acc) of a split plan; 0 for one chunk.
+size_t partial_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, const SplitPlan& sp) {
   if (sp.splits <= 1) return 0;
   const size_t rows = (size_t)B * Hq * sp.splits;
   return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
+}  // namespace
+
+extern "C" {
+
+size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
+  if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128) || num_splits < 0) return 0;
+  // enough for the bf16 and the FP8 entry points' plans
+  return std::max(partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, false)),
+                  partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, true)));
+}
+
 size_t attn_decode_fused_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
-  const size_t parts = attn_decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits);
+  if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128) || num_splits < 0) return 0;
+  const size_t parts = partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, true, false));
   if (parts == 0) return 0;
   return kDecodeCountBytes + parts;
 }
@@ -161,7 +196,7 @@ attn_status decode_common(const void* q, const void* k, const void* v, const flo
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (!q || !o || (Nk > 0 && (!k || !v))) return ATTN_ERR_INVALID;
   if (fp8 && Nk > 0 && (!k_scale || !v_scale)) return ATTN_ERR_INVALID;
-  SplitPlan sp = plan_splits(B, Hkv, Nk, num_splits);
+  SplitPlan sp = plan_splits(B, Hkv, Nk, d, num_splits, fused, fp8);
   attn::DecodeProblem p{};
   p.q = q;
   p.k = k;
@@ -177,8 +212,7 @@ attn_status decode_common(const void* q, const void* k, const void* v, const flo
   p.num_splits = sp.splits;
   p.chunk = sp.chunk;
   if (sp.splits > 1) {
-    const size_t need = fused ? attn_decode_fused_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
-                              : attn_decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits);
+    const size_t need = (fused ? kDecodeCountBytes : 0) + partial_bytes(B, Hq, Hkv, d, sp);
     if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     // the arrival counts take device atomics: 4-byte alignment
     if (fused && ((uintptr_t)workspace & 3) != 0) return ATTN_ERR_INVALID;

@@ -76,18 +76,25 @@ __device__ __forceinline__ float load_agent(const float* p) {
 
 // Fold the num_splits partial states of row (b, query head) for output
 // column col and write O (and LSE from column 0).  The merge kernel and the
-// single-launch path share it, so both give the same bits.
-template <int D>
+// single-launch path share it, so both give the same bits.  AGENT: the
+// states were written by this same launch on other XCDs (device-scope
+// loads); otherwise by an earlier kernel (plain loads, which may hit L2).
+// The loops are unrolled so that several loads are in flight at once.
+template <int D, bool AGENT>
 __device__ __forceinline__ void fold_split_states(const DecArgs& a, size_t row, int col) {
+  auto ld = [](const float* p) { return AGENT ? load_agent(p) : *p; };
   const float* ml = a.part_ml + row * a.S * 2;
+  const float* pa = a.part_acc + row * a.S * D + col;
   float M = kNegInf;
-  for (int s = 0; s < a.S; s++) M = fmaxf(M, load_agent(ml + 2 * s));
+#pragma unroll 8
+  for (int s = 0; s < a.S; s++) M = fmaxf(M, ld(ml + 2 * s));
   float L = 0.0f, A = 0.0f;
+#pragma unroll 8
   for (int s = 0; s < a.S; s++) {
-    const float ms = load_agent(ml + 2 * s);
+    const float ms = ld(ml + 2 * s);
     const float f = (ms == kNegInf) ? 0.0f : fast_exp2(ms - M);
-    L += f * load_agent(ml + 2 * s + 1);
-    A += f * load_agent(a.part_acc + (row * a.S + s) * D + col);
+    L += f * ld(ml + 2 * s + 1);
+    A += f * ld(pa + (size_t)s * D);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   a.o[row * D + col] = to_bf16(A * inv);
@@ -112,7 +119,7 @@ __device__ void merge_if_last(const DecArgs& a, int b, int kvh, int pair) {
   const int total = a.g * D;
   for (int e = threadIdx.x; e < total; e += kWaves * 64) {
     const int qh = e / D, col = e % D;
-    fold_split_states<D>(a, (size_t)b * a.Hq + kvh * a.g + qh, col);
+    fold_split_states<D, true>(a, (size_t)b * a.Hq + kvh * a.g + qh, col);
   }
   if (threadIdx.x == 0) atomicExch(a.counters + pair, 0u);
 }
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
   const int lane = threadIdx.x & 63;
   if (row >= a.B * a.Hq) return;
 #pragma unroll
-  for (int e = 0; e < D / 64; e++) fold_split_states<D>(a, (size_t)row, e * 64 + lane);
+  for (int e = 0; e < D / 64; e++) fold_split_states<D, false>(a, (size_t)row, e * 64 + lane);
 }
 
 template <int D>

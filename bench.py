@@ -22,8 +22,15 @@ packed batch of 16 sequences (attn_fwd_varlen); decode_fp8 = the decode shape
 over an FP8 E4M3 KV cache (attn_decode_splitkv_fp8); decode_fused = the decode
 shape in one launch (attn_decode_splitkv_fused, the last split merges).
 
+--sweep times every point the targets are stated for instead (forward causal
+N = 2048..44032 at 32 q / 8 kv heads and at B=4 H=16 N=2048, the backward, and
+the decode at 1/16/48 streams x 512..4096 keys with both decode entry points),
+one JSON line per point with median / p10 / p90 / min over >= 50 calls, inputs
+rotating over copies of >= 512 MiB so that no call finds them in the MALL.
+
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu]
                        [--paths fwd,decode,bwd[,varlen][,decode_fp8][,decode_fused]]
+       python bench.py --sweep
 """
 from __future__ import annotations
 
@@ -330,6 +337,120 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n * 4, "copy_probe_kib": n * 4 // 1024}), flush=True)
 
 
+# --sweep: every point the throughput targets are stated for, each timed on
+# its own with percentiles (fwd and bwd >= 50 % of bf16 MFMA at N >= 2048,
+# decode >= 70 % of HBM where its KV cache is >= 256 MiB)
+SWEEP_FWD = [(1, 32, 8, n) for n in (2048, 4096, 8192, 16384, 44032)] + [(4, 16, 16, 2048)]
+SWEEP_DECODE = [(b, n) for b in (1, 16, 48) for n in (512, 1024, 2048, 4096)]
+POOL_BYTES = 512 << 20  # inputs rotate over copies of at least this size (twice the 256 MB MALL)
+
+
+def time_calls(fn, n_inputs, warm=10, min_reps=50, min_ms=100.0):
+    """Per-call HIP-event times of fn(i) (i selects the input copy), after warm
+    untimed calls: at least min_reps calls and min_ms of GPU time.  Also the
+    wall clock over the timed loop with one synchronisation."""
+    import torch
+
+    for i in range(warm):
+        fn(i % n_inputs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn(0)
+    e1.record()
+    torch.cuda.synchronize()
+    reps = max(min_reps, int(min_ms / max(e0.elapsed_time(e1), 1e-3)) + 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(reps):
+        ev[r][0].record()
+        fn(r % n_inputs)
+        ev[r][1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / reps
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    pick = lambda f: ms[min(len(ms) - 1, int(f * len(ms)))]
+    mean = sum(ms) / len(ms)
+    return {"reps": reps, "ms_median": round(pick(0.5), 5), "ms_p10": round(pick(0.1), 5),
+            "ms_p90": round(pick(0.9), 5), "ms_min": round(ms[0], 5), "wall_ms": round(wall, 5),
+            "timers_agree": abs(wall - mean) <= 0.1 * mean + 0.01}
+
+
+def sweep():
+    import torch
+
+    import attention_online_softmax_attn_amd as am
+
+    gen = torch.Generator(device="cuda").manual_seed(8)
+    rnd = lambda *shape: torch.randn(*shape, device="cuda", generator=gen).to(torch.bfloat16)
+    lines = []
+
+    def emit(d):
+        lines.append(d)
+        print(json.dumps(d), flush=True)
+
+    for B, Hq, Hkv, N in SWEEP_FWD:
+        d = 128
+        per_copy = 2 * B * (Hq + 2 * Hkv) * N * d
+        n = max(1, -(-POOL_BYTES // per_copy))
+        qs = [(rnd(B, Hq, N, d), rnd(B, Hkv, N, d), rnd(B, Hkv, N, d)) for _ in range(n)]
+        o = torch.empty_like(qs[0][0])
+        lse = torch.empty(B, Hq, N, dtype=torch.float32, device="cuda")
+        t = time_calls(lambda i: am.attn_fwd(*qs[i], causal=True, out=o, lse=lse), n)
+        f = fwd_flops(B, Hq, N, N, d, True)
+        tf = f / t["ms_median"] / 1e9
+        emit({"path": "fwd", "shape": f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal", "copies": n, **t,
+              "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "target": 0.5,
+              "meets": tf / PEAK_BF16_TFLOPS >= 0.5})
+        del qs, o, lse
+    # backward at B=4 H=16 N=2048 (O and LSE from the forward, outside the timing)
+    c = BACKWARD
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    n = max(1, -(-POOL_BYTES // (2 * 5 * B * H * N * d)))
+    sets = []
+    for _ in range(n):
+        q, k, v, do = rnd(B, H, N, d), rnd(B, H, N, d), rnd(B, H, N, d), rnd(B, H, N, d)
+        o, lse = am.attn_fwd(q, k, v, causal=True)
+        sets.append((q, k, v, o, do, lse))
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty(B, H, N, d, **f32), torch.empty(B, H, N, d, **f32), torch.empty(B, H, N, d, **f32)
+    ws = torch.empty(am.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    t = time_calls(lambda i: am.attn_bwd(*sets[i], causal=True, workspace=ws, dq=dq, dk=dk, dv=dv), n)
+    f = bwd_flops(B, H, N, N, d, True)
+    tf = f / t["ms_median"] / 1e9
+    emit({"path": "bwd", "shape": f"B={B} H={H} N={N} d={d} causal", "copies": n, **t, "tflops": round(tf, 1),
+          "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "target": 0.5, "meets": tf / PEAK_BF16_TFLOPS >= 0.5})
+    del sets, dq, dk, dv
+    # decode, two launches and one
+    for B, L in SWEEP_DECODE:
+        Hq, Hkv, d = 32, 8, 128
+        kv = 2 * B * Hkv * L * d * 2
+        n = max(1, -(-POOL_BYTES // kv))
+        q = rnd(B, Hq, 1, d)
+        kvs = [(rnd(B, Hkv, L, d), rnd(B, Hkv, L, d)) for _ in range(n)]
+        o = torch.empty_like(q)
+        lse = torch.empty(B, Hq, 1, dtype=torch.float32, device="cuda")
+        ws2 = torch.empty(max(1, am.decode_workspace_bytes(B, Hq, Hkv, L, d, 0)), dtype=torch.uint8, device="cuda")
+        ws1 = torch.zeros(max(1, am.decode_fused_workspace_bytes(B, Hq, Hkv, L, d, 0)), dtype=torch.uint8,
+                          device="cuda")
+        b = decode_bytes(B, Hq, Hkv, L, d)
+        for name, fn in (("decode", lambda i: am.attn_decode_splitkv(q, *kvs[i], workspace=ws2, out=o, lse=lse)),
+                         ("decode_fused",
+                          lambda i: am.attn_decode_splitkv_fused(q, *kvs[i], workspace=ws1, out=o, lse=lse))):
+            t = time_calls(fn, n)
+            gbs = b / t["ms_median"] / 1e6
+            bound = kv >= (256 << 20)
+            emit({"path": name, "shape": f"{B} streams x {L} keys, Hq={Hq} Hkv={Hkv} d={d}",
+                  "splits": am.decode_num_splits(B, Hq, Hkv, L, d), "copies": n, **t, "gbs": round(gbs, 1),
+                  "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "target": 0.7 if bound else None,
+                  "meets": (gbs / PEAK_HBM_GBS >= 0.7) if bound else None})
+        del kvs
+    met = [x["meets"] for x in lines if x["meets"] is not None]
+    print(json.dumps({"sweep_points": len(lines), "targets": len(met), "targets_met": sum(met),
+                      "timers_agree": all(x["timers_agree"] for x in lines)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +459,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--paths", default="fwd,decode,bwd")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every target point (fwd N sweep, bwd, all decode points), one JSON line each")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -353,6 +476,9 @@ def main():
         sys.exit(1)
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.sweep:
+        sweep()
         return
     st, per, step_ms, wall = run_gpu(paths, args.steps, args.warmup)
 

@@ -104,8 +104,16 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
  * (0 = automatic plan); every chunk yields a partial state (m, l, acc) for the
  * Hq/Hkv query heads that share the kv head, written to the workspace, and a
  * merge kernel folds the partials with the monoid rule and writes o (dtype)
- * and lse (fp32, may be NULL).  Only ATTN_BF16 is built.  causal is accepted
+ * and lse (fp32, may be NULL).  With one chunk the single kernel writes o and
+ * lse and no workspace is used.  Only ATTN_BF16 is built.  causal is accepted
  * and has no effect (a single bottom-right-aligned query sees every key).
+ * attn_decode_num_splits returns the automatic plan: the power of two (1 to
+ * 64) that minimises a cost model of the decode (per-workgroup streaming rate,
+ * whole-device HBM rate, cost of each extra chunk and of the merge launch),
+ * so a chunk per (stream, kv head) from about 128 (stream, kv head) pairs up.
+ * attn_decode_workspace_bytes(..., num_splits) is enough for this entry point
+ * and for attn_decode_splitkv_fp8 (whose plan models the FP8 kernel) at the
+ * same num_splits.
  */
 int attn_decode_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d);
 size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits);
@@ -116,8 +124,8 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
 
 /*
  * Split-KV decode in one launch.  Same arguments, rules and result as
- * attn_decode_splitkv (the same kernels and the same fold, so the same bits),
- * but no merge kernel: each chunk's workgroup publishes its partial state
+ * attn_decode_splitkv for the same num_splits (the same kernels and the same
+ * fold, so the same bits), but no merge kernel: each chunk's workgroup publishes its partial state
  * and counts itself in for its (stream, kv head) with a device atomic, and
  * the last one to arrive folds every chunk's state and writes o and lse.
  * It folds the chunks in index order whichever finishes last, so the result
@@ -138,6 +146,9 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
  *             and memory used by another entry point must be zeroed again
  *             before it serves this one.
  */
+/* The automatic plan of this entry point: attn_decode_num_splits's model
+ * without the merge launch, so it may split where the two-launch path does not. */
+int attn_decode_fused_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d);
 size_t attn_decode_fused_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits);
 attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                                       int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,

@@ -181,14 +181,20 @@ def test_decode_fused_rejects(kw, code):
 @no_gpu
 def test_decode_fused_workspace_must_hold_the_counts():
     # exactly the two-launch workspace is too small: the counts come first
-    B, Hq, Hkv, L, d = 2, 32, 8, 4096, 128
-    need2 = am.decode_workspace_bytes(B, Hq, Hkv, L, d, 0)
-    assert decf(ws_bytes=need2) == am.ATTN_ERR_WORKSPACE
+    B, Hq, Hkv, L, d, S = 2, 32, 8, 4096, 128, 8
+    need2 = am.decode_workspace_bytes(B, Hq, Hkv, L, d, S)
+    assert decf(ws_bytes=need2, splits=S) == am.ATTN_ERR_WORKSPACE
+    assert decf(ws_bytes=am.decode_fused_workspace_bytes(B, Hq, Hkv, L, d, S) - 1, splits=S) == am.ATTN_ERR_WORKSPACE
     assert decf(ws_bytes=am.decode_fused_workspace_bytes(B, Hq, Hkv, L, d, 0) - 1) == am.ATTN_ERR_WORKSPACE
 
 
 def test_decode_fused_workspace_layout():
-    for B, L, s in [(1, 512, 0), (48, 4096, 0), (16, 4096, 3), (2, 4096, 1), (48, 4096, 128)]:
+    for B, L, s in [(1, 512, 4), (48, 4096, 2), (16, 4096, 3), (2, 4096, 1), (48, 4096, 128), (48, 4096, 0),
+                    (1, 4096, 0)]:
+        if s == 0:
+            s = am.decode_fused_num_splits(B, 32, 8, L, 128)   # the automatic plans of the two may differ
+            assert am.decode_fused_workspace_bytes(B, 32, 8, L, 128, 0) == am.decode_fused_workspace_bytes(
+                B, 32, 8, L, 128, s)
         two = am.decode_workspace_bytes(B, 32, 8, L, 128, s)
         one = am.decode_fused_workspace_bytes(B, 32, 8, L, 128, s)
         if two == 0:
@@ -238,13 +244,19 @@ def test_split_plan_and_workspace():
         s = n(B, 32, 8, L, 128)
         assert 1 <= s <= max(1, L // 32)
         ws = am.decode_workspace_bytes(B, 32, 8, L, 128, 0)
-        if s == 1:
-            assert ws == 0
-        else:
-            assert ws >= B * 32 * s * (128 + 2) * 4
-    # workgroup count B*Hkv*splits fills the 256 CUs in whole waves where it can
-    assert (48 * 8 * n(48, 32, 8, 4096, 128)) % 256 == 0
-    assert (16 * 8 * n(16, 32, 8, 4096, 128)) % 256 == 0
+        # enough for this plan (and the FP8 entry point's, which may split more)
+        assert ws >= (0 if s == 1 else B * 32 * s * (128 + 2) * 4)
+        assert am.decode_workspace_bytes(B, 32, 8, L, 128, 1) == 0
+    # the cost model: from 16 streams x 8 kv heads up the cache is streamed by
+    # enough workgroups without splitting; one stream splits into 8..32 chunks
+    # of its 4096 keys; plans are powers of two; the single-launch path, with
+    # no merge launch to pay for, splits at least as much
+    assert n(48, 32, 8, 4096, 128) == 1 and n(16, 32, 8, 4096, 128) == 1 and n(48, 32, 8, 512, 128) == 1
+    assert 8 <= n(1, 32, 8, 4096, 128) <= 32
+    for B in (1, 2, 4, 8, 16, 48):
+        for L in (1, 100, 512, 1024, 2048, 4096, 32768):
+            s, f = n(B, 32, 8, L, 128), am.decode_fused_num_splits(B, 32, 8, L, 128)
+            assert s & (s - 1) == 0 and f & (f - 1) == 0 and 1 <= s <= f <= 64
     # explicit split counts are honoured up to one split per 32-key tile
     assert am.decode_workspace_bytes(1, 4, 1, 100, 64, 7) == am.decode_workspace_bytes(1, 4, 1, 100, 64, 4)
     assert am.decode_workspace_bytes(1, 4, 1, 0, 64, 0) == 0

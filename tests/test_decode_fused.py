@@ -44,6 +44,8 @@ def test_fused_equals_two_launch(shape, splits):
     print(f"fused decode B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} splits={splits}", flush=True)
     q, k, v = _inputs(4000 + L + B, B, Hq, Hkv, L, d)
     qd, kd, vd = dev(q, True), dev(k, True), dev(v, True)
+    if splits == 0:
+        splits = am.decode_fused_num_splits(B, Hq, Hkv, L, d)  # the single-launch plan, for both
     o2, l2 = am.attn_decode_splitkv(qd, kd, vd, num_splits=splits)
     o1, l1 = am.attn_decode_splitkv_fused(qd, kd, vd, num_splits=splits)
     torch.cuda.synchronize()
@@ -83,6 +85,7 @@ def test_fused_workspace_is_reused_across_calls():
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for i, ((B, Hq, Hkv, L, d), splits) in enumerate(plan):
         print(f"reuse call {i}: B={B} L={L} splits={splits}", flush=True)
+        splits = splits or am.decode_fused_num_splits(B, Hq, Hkv, L, d)
         q, k, v = _inputs(4200 + i, B, Hq, Hkv, L, d)
         qd, kd, vd = dev(q, True), dev(k, True), dev(v, True)
         o1, l1 = am.attn_decode_splitkv_fused(qd, kd, vd, num_splits=splits, workspace=ws)
@@ -101,12 +104,12 @@ def test_fused_back_to_back_on_one_stream():
     import attention_online_softmax_attn_amd as am
     from gpu_helpers import dev
 
-    B, Hq, Hkv, L, d = 16, 32, 8, 4096, 128
+    B, Hq, Hkv, L, d, S = 16, 32, 8, 4096, 128, 4
     q, k, v = _inputs(4300, B, Hq, Hkv, L, d)
     qd, kd, vd = dev(q, True), dev(k, True), dev(v, True)
-    ws = torch.zeros(am.decode_fused_workspace_bytes(B, Hq, Hkv, L, d, 0), dtype=torch.uint8, device="cuda")
-    ref_o, ref_l = am.attn_decode_splitkv(qd, kd, vd)
-    outs = [am.attn_decode_splitkv_fused(qd, kd, vd, workspace=ws) for _ in range(8)]
+    ws = torch.zeros(am.decode_fused_workspace_bytes(B, Hq, Hkv, L, d, S), dtype=torch.uint8, device="cuda")
+    ref_o, ref_l = am.attn_decode_splitkv(qd, kd, vd, num_splits=S)
+    outs = [am.attn_decode_splitkv_fused(qd, kd, vd, num_splits=S, workspace=ws) for _ in range(8)]
     torch.cuda.synchronize()
     assert _counts_zero(ws)
     for o, lse in outs:
