@@ -141,7 +141,43 @@ def test_no_writes_outside_outputs():
     assert guards_intact(ofull, o.numel()) and guards_intact(lfull, lse.numel())
 
 
-# ---------------------------------------------------------------- large grids (the 8-wave ping-pong kernel)
+# ---------------------------------------------------------------- the 4-wave configuration at scale
+# The launcher runs the 8-wave kernel for at least 2048 query tiles of 256
+# rows and the 4-wave kernel below that; the small shapes above take the
+# 4-wave kernel with few workgroups, these with many (up to 1024 tiles of
+# 128 rows), ragged and with Nq != Nk, on sampled rows.
+MIDDLE = [
+    # B, Hq, Hkv, Nq, Nk, d, expected configuration
+    (4, 16, 16, 2048, 2048, 128, "4-wave"),
+    (2, 32, 8, 1100, 1300, 64, "4-wave"),
+    (1, 32, 8, 2048, 2048, 128, "4-wave"),
+    (1, 16, 4, 4000, 3900, 128, "4-wave"),
+]
+
+
+def _config(B, Hq, Nq):
+    return "8-wave" if B * Hq * ((Nq + 255) // 256) >= 2048 else "4-wave"
+
+
+@pytest.mark.parametrize("shape", MIDDLE)
+@pytest.mark.parametrize("causal", [True, False])
+def test_middle_grid_sampled_rows(oracle_mod, shape, causal):
+    B, Hq, Hkv, Nq, Nk, d, cfg = shape
+    assert _config(B, Hq, Nq) == cfg
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = synth.attn_inputs(700 + Nq + d, B, Hq, Hkv, Nq, Nk, d, bf16=True)
+    print(f"middle case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} ({cfg})", flush=True)
+    o, lse = attn_fwd(dev(q, True), dev(k, True), dev(v, True), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    forced = (0, 1, 63, 64, 127, 128, 129, Nq // 2, Nq - 65, Nq - 2, Nq - 1)
+    rows = synth.sample_rows(40007 + Nq, 192, B, Hq, Nq, forced_i=forced)
+    eo, el = oracle_mod.fwd_rows(q, k, v, rows, scale, causal)
+    idx = (rows[:, 0], rows[:, 1], rows[:, 2])
+    assert_close("O sampled", host(o[idx[0], idx[1], idx[2]]), eo, TOL_O_BF16)
+    assert_close("LSE sampled", host(lse[idx[0], idx[1], idx[2]]), el, TOL_LSE_BF16)
+
+
+# ---------------------------------------------------------------- large grids (the 8-wave kernel)
 # Problems with at least 8 workgroups of 256 query rows per CU (>= 2048 of
 # them) run the 8-wave kernel; these shapes reach it with ragged lengths,
 # grouped-query heads and Nq != Nk, checked on sampled rows (the oracle of a
