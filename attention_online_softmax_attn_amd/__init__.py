@@ -10,6 +10,7 @@ not built, or a tensor is not on the GPU, these functions raise.
     attn_decode_splitkv(q, k, v, scale, num_splits=0) -> (o, lse)
     attn_decode_splitkv_fused(q, k, v, scale, num_splits=0)  -> (o, lse)
     attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, ...) -> (o, lse)
+    attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len) -> (o, lse)
     attn_bwd(q, k, v, o, dout, lse, causal, scale)    -> (dq, dk, dv)
 
 Layouts are [B, H, N, d] contiguous (q/o/dout/dq with Hq heads, k/v/dk/dv with
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_fused_workspace_bytes.restype = sz
     L.attn_decode_splitkv_fused.argtypes = L.attn_decode_splitkv.argtypes
     L.attn_decode_splitkv_fused.restype = ci
+    L.attn_decode_paged.argtypes = [vp] * 7 + [i64] * 8 + [f32, ci, vp, sz, vp]
+    L.attn_decode_paged.restype = ci
     L.attn_decode_splitkv_fp8.argtypes = [vp] * 7 + [i64] * 6 + [f32, ci, vp, sz, vp]
     L.attn_decode_splitkv_fp8.restype = ci
     L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
@@ -259,6 +262,42 @@ def attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, scale=None, num_splits:
                                        int(num_splits), _ptr(workspace), ws_bytes, _stream())
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_splitkv_fp8")
+    return o, (lse if want_lse else None)
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale=None, num_splits: int = 0,
+                      workspace=None, out=None, lse=None, want_lse: bool = True):
+    """Split-KV decode over a paged bf16 KV cache.  q [B, Hq, 1, d]; k_cache,
+    v_cache [num_pages, Hkv, page_size, d]; block_table int32 [B, max_pages];
+    seq_lens int32 [B]; max_seq_len >= every seq_lens entry.  Returns
+    (o [B, Hq, 1, d], lse [B, Hq, 1])."""
+    _check_dev(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, Hq, 1, d] and k_cache, v_cache [num_pages, Hkv, page_size, d]")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("q, k_cache and v_cache must be bfloat16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or block_table.dim() != 2:
+        raise TypeError("block_table must be int32 [B, max_pages] and seq_lens int32 [B]")
+    B, Hq, Nq, d = q.shape
+    num_pages, Hkv, page, _ = k_cache.shape
+    if k_cache.shape[3] != d or block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, the cache, block_table and seq_lens")
+    for t in (q, k_cache, v_cache, block_table, seq_lens):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, int(max_seq_len), d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(o),
+                                 _ptr(lse) if want_lse else None, B, Hq, Hkv, d, num_pages, page,
+                                 block_table.shape[1], int(max_seq_len), _scale(scale, d), int(num_splits),
+                                 _ptr(workspace), ws_bytes, _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_paged")
     return o, (lse if want_lse else None)
 
 

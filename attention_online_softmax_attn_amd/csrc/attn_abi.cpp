@@ -257,6 +257,58 @@ attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* 
                        workspace, workspace_bytes, dtype, stream);
 }
 
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                              int64_t d, int64_t num_pages, int64_t page_size, int64_t max_pages,
+                              int64_t max_seq_len, float scale, int num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (num_pages < 0 || page_size < 0 || max_pages < 0 || max_seq_len < 0) return ATTN_ERR_INVALID;
+  attn_status st = check_common(B, Hq, Hkv, 1, max_seq_len, d, scale, ATTN_BF16);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0) return ATTN_ERR_INVALID;
+  if (page_size == 0 || page_size % attn::kDecodeTile != 0) return ATTN_ERR_UNSUPPORTED;
+  if (max_pages > ATTN_MAX_SEQ / page_size) return ATTN_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 32) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0) return ATTN_OK;
+  if (!q || !o || !seq_lens) return ATTN_ERR_INVALID;
+  // keys can be read only if there are pages to read them from
+  if (max_seq_len > 0 && (max_pages == 0 || num_pages == 0 || !k_cache || !v_cache || !block_table))
+    return ATTN_ERR_INVALID;
+  SplitPlan sp = plan_splits(B, Hkv, max_seq_len, d, num_splits, false, false);
+  attn::DecodeProblem p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nk = max_seq_len;
+  p.d = d;
+  p.scale = scale;
+  p.num_splits = sp.splits;
+  p.chunk = sp.chunk;
+  if (sp.splits > 1) {
+    const size_t need = partial_bytes(B, Hq, Hkv, d, sp);
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t rows = (size_t)B * Hq * sp.splits;
+    p.part_acc = (float*)workspace;
+    p.part_ml = (float*)((char*)workspace + align256(rows * d * sizeof(float)));
+  }
+  if (max_seq_len > 0) {
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.page = page_size;
+    p.max_pages = max_pages;
+    p.num_pages = num_pages;
+  } else {
+    // no keys at all: the dense kernel with Nk = 0 writes O = 0, LSE = -inf
+    p.k = p.v = nullptr;
+  }
+  return attn::launch_decode(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_decode_splitkv_fp8(const void* q, const void* k, const void* v, const float* k_scale,
                                     const float* v_scale, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
                                     int64_t Nq, int64_t Nk, int64_t d, float scale, int num_splits, void* workspace,

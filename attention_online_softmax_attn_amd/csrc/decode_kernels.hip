@@ -59,6 +59,12 @@ struct DecArgs {
   // single-launch mode (null: a merge kernel folds the splits): one arrival
   // count per (stream, kv head), zero on entry and left zero on exit
   unsigned* counters;
+  // paged KV cache (null for a dense one): k, v are [num_pages, Hkv, page, D];
+  // key j of stream b sits in slot j % page of page block_table[b][j / page];
+  // stream b has seq_lens[b] keys (Nk is the longest)
+  const int* block_table;
+  const int* seq_lens;
+  int page, max_pages, num_pages;
 };
 
 // The partial states are written and, in single-launch mode, read back by
@@ -124,7 +130,7 @@ __device__ void merge_if_last(const DecArgs& a, int b, int kvh, int pair) {
   if (threadIdx.x == 0) atomicExch(a.counters + pair, 0u);
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs a) {
   constexpr int BN = kDecodeTile;
   constexpr int TILE_BYTES = BN * D * 2;
@@ -146,14 +152,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   const int b = pair / a.Hkv;
   const int kvh = pair % a.Hkv;
 
+  // this stream's keys: all Nk, or (paged) its own length, clamped to the
+  // block table's reach
+  int nk_b = a.Nk;
+  if constexpr (PAGED) nk_b = min(max(a.seq_lens[b], 0), min(a.Nk, a.max_pages * a.page));
   const int k0 = split * a.chunk;
-  const int k1 = min(a.Nk, k0 + a.chunk);
+  const int k1 = min(nk_b, k0 + a.chunk);
   const int n_tiles = k1 > k0 ? (k1 - k0 + BN - 1) / BN : 0;
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
 
   const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)a.Nk * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)a.Nk * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (PAGED ? 0 : kv_head), (uint32_t)a.Nk * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (PAGED ? 0 : kv_head), (uint32_t)a.Nk * D * 2);
   const size_t q_grp = ((size_t)b * a.Hq + (size_t)kvh * a.g) * D;  // the g query rows of this kv head
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_grp, (uint32_t)a.g * D * 2);
 
@@ -161,14 +171,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
 
   auto issue = [&](int i, char* kt, char* vt) {
     const int j0 = k0 + (wave + kWaves * i) * BN;
+    __amdgpu_buffer_rsrc_t tk = rk, tv = rv;
+    int row0 = j0;
+    if constexpr (PAGED) {
+      // one 32-key tile lies in one page (page is a multiple of 32); rows
+      // past this stream's keys read as zeros, and a page id outside the
+      // cache is clamped into it
+      const int pg = min(max(a.block_table[(size_t)b * a.max_pages + j0 / a.page], 0), a.num_pages - 1);
+      const size_t base = (((size_t)pg * a.Hkv + kvh) * a.page + (j0 % a.page)) * D;
+      const uint32_t bytes = (uint32_t)min(BN, k1 - j0) * D * 2;
+      tk = make_rsrc(a.k + base, bytes);
+      tv = make_rsrc(a.v + base, bytes);
+      row0 = 0;
+    }
 #pragma unroll
     for (int n = 0; n < LOADS; n++) {
       const int p = n * 64 + lane;
       const int r = p / CPR;
       const int cc = (p % CPR) ^ swz<D>(r);
-      const uint32_t src = (uint32_t)(((j0 + r) * D + cc * 8) * 2);
-      buf_load_lds16(rk, src, (lds_void*)(kt + n * 1024));
-      buf_load_lds16(rv, src, (lds_void*)(vt + n * 1024));
+      const uint32_t src = (uint32_t)(((row0 + r) * D + cc * 8) * 2);
+      buf_load_lds16(tk, src, (lds_void*)(kt + n * 1024));
+      buf_load_lds16(tv, src, (lds_void*)(vt + n * 1024));
     }
   };
 
@@ -545,10 +568,17 @@ hipError_t launch(const DecodeProblem& p, hipStream_t s) {
   a.k_scale = p.k_scale;
   a.v_scale = p.v_scale;
   a.counters = p.counters;
-  if (p.k8 != nullptr)
+  a.block_table = p.block_table;
+  a.seq_lens = p.seq_lens;
+  a.page = (int)p.page;
+  a.max_pages = (int)p.max_pages;
+  a.num_pages = (int)p.num_pages;
+  if (p.block_table != nullptr)
+    hipLaunchKernelGGL((decode_partial_kernel<D, true>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
+  else if (p.k8 != nullptr)
     hipLaunchKernelGGL((decode_partial_fp8_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_partial_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((decode_partial_kernel<D, false>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.S == 1 || a.counters != nullptr) return e;
   const int rows = a.B * a.Hq;

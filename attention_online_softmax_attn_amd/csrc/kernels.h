@@ -51,6 +51,13 @@ struct DecodeProblem {
   // arrival counts, zero on entry; the last split of each (stream, kv head)
   // to finish merges them and returns its count to zero
   unsigned* counters = nullptr;
+  // paged KV cache (bf16; null block_table for a dense one): k, v are
+  // [num_pages, Hkv, page, d] with page a multiple of kDecodeTile; block_table
+  // [B, max_pages] int32 page ids, seq_lens [B] int32 keys per stream; Nk is
+  // the longest stream (it sizes the split plan)
+  const int32_t* block_table = nullptr;
+  const int32_t* seq_lens = nullptr;
+  int64_t page = 0, max_pages = 0, num_pages = 0;
 };
 // Keys per decode tile; split chunks are whole multiples of it.
 constexpr int kDecodeTile = 32;

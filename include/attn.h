@@ -49,7 +49,10 @@
 extern "C" {
 #endif
 
-#define ATTN_MAX_SEQ (1 << 24)
+/* Longest sequence (Nq, Nk, packed totals): one head's rows of q, k or v
+ * then span at most 2^22 * 128 * 2 bytes = 1 GiB, so the kernels' 32-bit
+ * buffer offsets never overflow. */
+#define ATTN_MAX_SEQ (1 << 22)
 
 typedef enum {
   ATTN_OK = 0,
@@ -154,6 +157,36 @@ attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* 
                                       int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
                                       int causal, int num_splits, void* workspace, size_t workspace_bytes,
                                       attn_dtype dtype, void* stream);
+
+/*
+ * Split-KV decode over a paged KV cache, each stream with its own length.
+ * The decode of attn_decode_splitkv (one query token per stream, all of the
+ * stream's keys visible), with the cache held in pages as serving engines
+ * keep it: the second page ("Tang Project Derives GPU Kernels via IR ...",
+ * section "Details") measures decode over 16-48 concurrent streams.
+ *   Cache    k_cache, v_cache: bf16 [num_pages, Hkv, page_size, d]; a page
+ *            holds page_size consecutive keys of every kv head.  page_size
+ *            must be a multiple of 32 (ATTN_ERR_UNSUPPORTED otherwise).
+ *   Table    block_table: device int32 [B, max_pages]; key j of stream b is
+ *            slot j % page_size of page block_table[b * max_pages + j /
+ *            page_size].  Page ids outside [0, num_pages) are clamped into
+ *            it, so no access leaves the cache (the result is then wrong).
+ *   Lengths  seq_lens: device int32 [B]; stream b has seq_lens[b] keys,
+ *            clamped to [0, min(max_seq_len, max_pages * page_size)].  Keys
+ *            past a stream's length are never read, so unused slots and
+ *            pages may hold anything.  max_seq_len (host) must be at least
+ *            every seq_lens entry; it sizes the split plan and the
+ *            workspace, attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len,
+ *            d, num_splits).  A stream with no keys gets O = 0, LSE = -inf.
+ *   Other    q, o bf16 [B, Hq, 1, d]; lse fp32 [B, Hq] (may be NULL);
+ *            max_pages * page_size <= ATTN_MAX_SEQ; every other rule as
+ *            attn_decode_splitkv.
+ */
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                              int64_t d, int64_t num_pages, int64_t page_size, int64_t max_pages,
+                              int64_t max_seq_len, float scale, int num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * Split-KV decode over an FP8 KV cache: k and v hold OCP FP8 E4M3 codes

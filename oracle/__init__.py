@@ -210,6 +210,32 @@ def decode_fp8(q, k8, v8, k_scale, v_scale, scale: float):
     return o, lse
 
 
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float):
+    """One decode query per stream against a paged cache: stream b's keys are
+    j = 0 .. seq_lens[b] - 1, key j in slot j % P of page block_table[b, j // P]
+    (P the page size), cache layout [num_pages, Hkv, P, d]; every key visible.
+    The stream's keys are gathered into a dense [1, Hkv, L, d] history and
+    solved with fwd above; a stream with no keys gets O = 0, LSE = -inf.
+    Returns (O [B,Hq,1,d], LSE [B,Hq,1])."""
+    q = _f32(q)
+    kc, vc = np.asarray(k_cache), np.asarray(v_cache)
+    bt, sl = np.asarray(block_table), np.asarray(seq_lens)
+    B, Hq, Nq, d = q.shape
+    P = kc.shape[2]
+    o = np.zeros((B, Hq, Nq, d))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        L = int(sl[b])
+        if L <= 0:
+            continue
+        j = np.arange(L)
+        pages, slots = bt[b, j // P], j % P
+        k = np.ascontiguousarray(kc[pages, :, slots, :].transpose(1, 0, 2)[None])  # [1, Hkv, L, d]
+        v = np.ascontiguousarray(vc[pages, :, slots, :].transpose(1, 0, 2)[None])
+        o[b:b + 1], lse[b:b + 1] = fwd(q[b:b + 1], k, v, scale, False)
+    return o, lse
+
+
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel regions use."""
     return int(lib().oracle_num_threads())

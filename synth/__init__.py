@@ -143,3 +143,29 @@ def fp8_kv_inputs(seed: int, B: int, Hq: int, Hkv: int, Nk: int, d: int):
     k8 = np.stack([quantize_e4m3(k[:, h], ks[h]) for h in range(Hkv)], axis=1)
     v8 = np.stack([quantize_e4m3(v[:, h], vs[h]) for h in range(Hkv)], axis=1)
     return q, k8, v8, ks, vs
+
+
+def paged_kv_inputs(seed: int, lens, Hq: int, Hkv: int, page: int, d: int, spare_pages: int = 3):
+    """Decode inputs over a paged cache: q bf16-exact [B,Hq,1,d] and a cache
+    K, V [num_pages, Hkv, page, d] drawn as normal(seed, ...) draws them (q,
+    K, V), a block table int32 [B, max_pages] that gives each stream
+    ceil(len / page) distinct pages in a random order (from a generator
+    separate from the data's; entries past a stream's pages are -1), the
+    int32 lengths, and used [num_pages, page]: True where a slot holds one of
+    some stream's keys (callers may poison the rest)."""
+    lens = [int(x) for x in lens]
+    need = [(n + page - 1) // page for n in lens]
+    num_pages = sum(need) + spare_pages
+    max_pages = max(1, max(need) if need else 1)
+    q, kc, vc = normal(seed, [(len(lens), Hq, 1, d), (num_pages, Hkv, page, d), (num_pages, Hkv, page, d)], True)
+    rng = np.random.default_rng(seed + 7919)
+    perm = rng.permutation(num_pages)
+    table = np.full((len(lens), max_pages), -1, np.int32)
+    used = np.zeros((num_pages, page), bool)
+    at = 0
+    for b, (n, m) in enumerate(zip(lens, need)):
+        table[b, :m] = perm[at:at + m]
+        for j in range(m):
+            used[perm[at + j], :min(page, n - j * page)] = True
+        at += m
+    return q, kc, vc, table, np.asarray(lens, np.int32), used

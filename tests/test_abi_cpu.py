@@ -23,6 +23,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_varlen", "attn_decode_splitkv", "attn_decode_splitkv_fp8", "attn_bwd",
               "attn_decode_splitkv_fused", "attn_decode_fused_workspace_bytes", "attn_decode_workspace_bytes",
+              "attn_decode_paged",
               "attn_bwd_workspace_bytes", "attn_decode_num_splits", "attn_strerror"):
         assert n in names
 
@@ -78,7 +79,7 @@ def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.1
         (dict(dt=7), am.ATTN_ERR_INVALID),
         (dict(d=96), am.ATTN_ERR_UNSUPPORTED),
         (dict(d=256), am.ATTN_ERR_UNSUPPORTED),
-        (dict(Nk=(1 << 24) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(Nk=(1 << 22) + 1), am.ATTN_ERR_UNSUPPORTED),
     ],
 )
 def test_fwd_rejects(kw, code):
@@ -115,9 +116,9 @@ def fwd_varlen(q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, n=3, tq=300, tk=500, maxq=
         (dict(dt=9), am.ATTN_ERR_INVALID),
         (dict(dt=am.ATTN_F32), am.ATTN_ERR_UNSUPPORTED),
         (dict(d=96), am.ATTN_ERR_UNSUPPORTED),
-        (dict(tq=(1 << 24) + 1), am.ATTN_ERR_UNSUPPORTED),
-        (dict(tk=(1 << 24) + 1), am.ATTN_ERR_UNSUPPORTED),
-        (dict(maxq=(1 << 24) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(tq=(1 << 22) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(tk=(1 << 22) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(maxq=(1 << 22) + 1), am.ATTN_ERR_UNSUPPORTED),
     ],
 )
 def test_fwd_varlen_rejects(kw, code):
@@ -201,6 +202,43 @@ def test_decode_fused_workspace_layout():
             assert one == 0                       # one chunk: no partials, no counts
         else:
             assert one == two + 65536                # a fixed region of arrival counts first
+
+
+def decp(q=P, k=P, v=P, bt=P, sl=P, o=P, lse=P, B=4, Hq=32, Hkv=8, d=128, pages=100, page=64, maxp=20,
+         maxl=1280, scale=0.088, splits=0, ws=P, ws_bytes=1 << 30):
+    return am.lib().attn_decode_paged(q, k, v, bt, sl, o, lse, B, Hq, Hkv, d, pages, page, maxp, maxl, scale, splits,
+                                      ws, ws_bytes, None)
+
+
+@no_gpu
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(page=48), am.ATTN_ERR_UNSUPPORTED),                 # not a multiple of 32
+        (dict(page=0), am.ATTN_ERR_UNSUPPORTED),
+        (dict(page=-32), am.ATTN_ERR_INVALID),
+        (dict(maxp=(1 << 22) // 64 + 1), am.ATTN_ERR_UNSUPPORTED),  # reach above the longest sequence
+        (dict(maxl=(1 << 22) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(sl=NUL), am.ATTN_ERR_INVALID),
+        (dict(bt=NUL), am.ATTN_ERR_INVALID),
+        (dict(k=NUL), am.ATTN_ERR_INVALID),
+        (dict(pages=0), am.ATTN_ERR_INVALID),
+        (dict(maxp=0), am.ATTN_ERR_INVALID),
+        (dict(q=NUL), am.ATTN_ERR_INVALID),
+        (dict(Hq=30), am.ATTN_ERR_INVALID),
+        (dict(d=80), am.ATTN_ERR_UNSUPPORTED),
+        (dict(splits=-1), am.ATTN_ERR_INVALID),
+        (dict(splits=4, ws=NUL), am.ATTN_ERR_WORKSPACE),
+        (dict(splits=4, ws_bytes=16), am.ATTN_ERR_WORKSPACE),
+    ],
+)
+def test_decode_paged_rejects(kw, code):
+    assert decp(**kw) == code
+
+
+@no_gpu
+def test_decode_paged_empty_batch_launches_nothing():
+    assert decp(q=NUL, k=NUL, v=NUL, bt=NUL, sl=NUL, o=NUL, lse=NUL, B=0) == am.ATTN_OK
 
 
 def dec8(q=P, k=P, v=P, ks=P, vs=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scale=0.088, splits=0,
