@@ -82,6 +82,16 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int request
   return {eff, (int)chunk};
 }
 
+// The paged decode's plan.  Streams of unequal length leave whole-length
+// chunks unbalanced (the longest stream's run decides the end): from 2048
+// keys on the automatic plan takes at least two chunks, which measured 1-15 %
+// faster at 48 streams of 512..4096, 4096 and 64..8192 keys.
+SplitPlan paged_plan(int64_t B, int64_t Hkv, int64_t max_seq_len, int64_t d, int requested) {
+  if (requested == 0 && max_seq_len >= 2048)
+    requested = std::max(2, plan_splits(B, Hkv, max_seq_len, d, 0, false, false).splits);
+  return plan_splits(B, Hkv, max_seq_len, d, requested, false, false);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // The single-launch decode's arrival counts: a fixed region at the start of
@@ -167,9 +177,10 @@ extern "C" {
 
 size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
   if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128) || num_splits < 0) return 0;
-  // enough for the bf16 and the FP8 entry points' plans
-  return std::max(partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, false)),
-                  partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, true)));
+  // enough for the bf16, FP8 and paged entry points' plans
+  return std::max({partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, false)),
+                   partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, true)),
+                   partial_bytes(B, Hq, Hkv, d, paged_plan(B, Hkv, Nk, d, num_splits))});
 }
 
 size_t attn_decode_fused_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
@@ -274,7 +285,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   // keys can be read only if there are pages to read them from
   if (max_seq_len > 0 && (max_pages == 0 || num_pages == 0 || !k_cache || !v_cache || !block_table))
     return ATTN_ERR_INVALID;
-  SplitPlan sp = plan_splits(B, Hkv, max_seq_len, d, num_splits, false, false);
+  SplitPlan sp = paged_plan(B, Hkv, max_seq_len, d, num_splits);
   attn::DecodeProblem p{};
   p.q = q;
   p.k = k_cache;

@@ -169,6 +169,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
 
   char* wbase = smem + wave * 2 * STAGE;
 
+  // paged: the page ids of this chunk's first 64 pages, one per lane, loaded
+  // once so that a tile's address needs no memory round trip
+  int pg_first = 0, pg_lane = 0;
+  if constexpr (PAGED) {
+    pg_first = k0 / a.page;
+    const int npg = k1 > k0 ? (k1 - 1) / a.page - pg_first + 1 : 0;
+    if (lane < npg) pg_lane = a.block_table[(size_t)b * a.max_pages + pg_first + lane];
+  }
+
   auto issue = [&](int i, char* kt, char* vt) {
     const int j0 = k0 + (wave + kWaves * i) * BN;
     __amdgpu_buffer_rsrc_t tk = rk, tv = rv;
@@ -177,7 +186,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
       // one 32-key tile lies in one page (page is a multiple of 32); rows
       // past this stream's keys read as zeros, and a page id outside the
       // cache is clamped into it
-      const int pg = min(max(a.block_table[(size_t)b * a.max_pages + j0 / a.page], 0), a.num_pages - 1);
+      const int pi = j0 / a.page - pg_first;
+      const int id = pi < 64 ? __builtin_amdgcn_readlane(pg_lane, pi)
+                             : a.block_table[(size_t)b * a.max_pages + j0 / a.page];
+      const int pg = min(max(id, 0), a.num_pages - 1);
       const size_t base = (((size_t)pg * a.Hkv + kvh) * a.page + (j0 % a.page)) * D;
       const uint32_t bytes = (uint32_t)min(BN, k1 - j0) * D * 2;
       tk = make_rsrc(a.k + base, bytes);

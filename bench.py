@@ -20,7 +20,9 @@ cpu_baseline = the CPU oracle on a bounded sample of the same step's work
 Opt-in paths (not part of the default step): varlen = chunked prefill of a
 packed batch of 16 sequences (attn_fwd_varlen); decode_fp8 = the decode shape
 over an FP8 E4M3 KV cache (attn_decode_splitkv_fp8); decode_fused = the decode
-shape in one launch (attn_decode_splitkv_fused, the last split merges).
+shape in one launch (attn_decode_splitkv_fused, the last split merges);
+decode_paged = 48 streams of 512..4096 keys each (seeded) in a paged cache of
+64-key pages through a block table (attn_decode_paged).
 
 --sweep times every point the targets are stated for instead (forward causal
 N = 2048..44032 at 32 q / 8 kv heads and at B=4 H=16 N=2048, the backward, and
@@ -29,7 +31,7 @@ one JSON line per point with median / p10 / p90 / min over >= 50 calls, inputs
 rotating over copies of >= 512 MiB so that no call finds them in the MALL.
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu]
-                       [--paths fwd,decode,bwd[,varlen][,decode_fp8][,decode_fused]]
+                       [--paths fwd,decode,bwd[,varlen][,decode_fp8][,decode_fused][,decode_paged]]
        python bench.py --sweep
 """
 from __future__ import annotations
@@ -54,6 +56,8 @@ BACKWARD = dict(B=4, H=16, N=2048, d=128, causal=True, seed=5)
 # opt-in path (--paths ...,varlen): chunked prefill of 16 sequences, each
 # appending 512..2048 new tokens to a cached history of 0..4096 tokens
 VARLEN = dict(n=16, lq=(512, 2048), hist=(0, 4096), Hq=32, Hkv=8, d=128, seed=6, len_seed=7)
+# opt-in path (--paths ...,decode_paged): 48 streams of unequal length in 64-key pages
+PAGED = dict(B=48, Hq=32, Hkv=8, lens=(512, 4096), page=64, d=128, seed=9, len_seed=10)
 
 
 CSRC = os.path.join(ROOT, "attention_online_softmax_attn_amd", "csrc")
@@ -154,6 +158,16 @@ def setup(paths):
         q, k8, v8, ks, vs = synth.fp8_kv_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["L"], c["d"])
         st["decode_fp8"] = (to_dev(q), torch.from_numpy(k8).cuda(), torch.from_numpy(v8).cuda(),
                             torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda())
+    if "decode_paged" in paths:
+        import numpy as np
+        import torch
+
+        c = PAGED
+        lens = np.random.default_rng(c["len_seed"]).integers(c["lens"][0], c["lens"][1] + 1, size=c["B"])
+        q, kc, vc, table, lens_a, _ = synth.paged_kv_inputs(c["seed"], lens, c["Hq"], c["Hkv"], c["page"], c["d"])
+        st["decode_paged"] = (to_dev(q), to_dev(kc), to_dev(vc), torch.from_numpy(table).cuda(),
+                              torch.from_numpy(lens_a).cuda(), int(lens_a.max()))
+        st["decode_paged_lens"] = [int(x) for x in lens_a]
     if "varlen" in paths:
         import torch
 
@@ -204,6 +218,12 @@ def run_gpu(paths, steps, warmup):
         # the arrival counts start at zero; every call leaves them zero
         dev_out["decode_fused"] = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"),
                                    torch.zeros(max(ws, 1), dtype=torch.uint8, device="cuda"))
+    if "decode_paged" in paths:
+        q = st["decode_paged"][0]
+        c = PAGED
+        ws = am.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], st["decode_paged"][5], c["d"], 0)
+        dev_out["decode_paged"] = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"),
+                                   torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda"))
     if "varlen" in paths:
         q = st["varlen"][0]
         dev_out["varlen"] = (torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda"))
@@ -226,6 +246,10 @@ def run_gpu(paths, steps, warmup):
             q, k, v = st["decode_fused"]
             o, lse, ws = dev_out["decode_fused"]
             am.attn_decode_splitkv_fused(q, k, v, workspace=ws, out=o, lse=lse)
+        elif name == "decode_paged":
+            q, kc, vc, bt, sl, ml = st["decode_paged"]
+            o, lse, ws = dev_out["decode_paged"]
+            am.attn_decode_paged(q, kc, vc, bt, sl, ml, workspace=ws, out=o, lse=lse)
         elif name == "varlen":
             q, k, v, cq, ck, mq = st["varlen"]
             o, lse = dev_out["varlen"]
@@ -235,7 +259,7 @@ def run_gpu(paths, steps, warmup):
             o, lse, dq, dk, dv, ws = dev_out["bwd"]
             am.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
 
-    order = [p for p in ("fwd", "decode", "bwd", "decode_fp8", "decode_fused", "varlen") if p in paths]
+    order = [p for p in ("fwd", "decode", "bwd", "decode_fp8", "decode_fused", "decode_paged", "varlen") if p in paths]
     for _ in range(warmup):
         for p in order:
             run_path(p)
@@ -525,6 +549,16 @@ def main():
                                      "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
                                      "shape": "48 streams, Hq=32 Hkv=8 d=128, 4096 keys, one launch"}
         total_flops += decode_flops(c["B"], c["Hq"], c["L"], c["d"])
+    if "decode_paged" in paths:
+        c = PAGED
+        lens = st["decode_paged_lens"]
+        b = sum(2.0 * c["Hkv"] * n * c["d"] * 2 for n in lens) + 2.0 * c["B"] * c["Hq"] * c["d"] * 2 + c["B"] * c["Hq"] * 4
+        t = sum(per["decode_paged"]) / len(per["decode_paged"])
+        out_paths["decode_paged"] = {"ms": round(t, 4), "ms_median": round(med(per["decode_paged"]), 4),
+                                     "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
+                                     "shape": f"48 streams of 512..4096 keys ({sum(lens)} in all), 64-key pages, "
+                                              "Hq=32 Hkv=8 d=128"}
+        total_flops += sum(decode_flops(1, c["Hq"], n, c["d"]) for n in lens)
     if "varlen" in paths:
         c = VARLEN
         lens_q, lens_k = st["varlen_lens"]

@@ -114,9 +114,9 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
  * 64) that minimises a cost model of the decode (per-workgroup streaming rate,
  * whole-device HBM rate, cost of each extra chunk and of the merge launch),
  * so a chunk per (stream, kv head) from about 128 (stream, kv head) pairs up.
- * attn_decode_workspace_bytes(..., num_splits) is enough for this entry point
- * and for attn_decode_splitkv_fp8 (whose plan models the FP8 kernel) at the
- * same num_splits.
+ * attn_decode_workspace_bytes(..., num_splits) is enough for this entry point,
+ * for attn_decode_splitkv_fp8 (whose plan models the FP8 kernel) and for
+ * attn_decode_paged (Nk = its max_seq_len) at the same num_splits.
  */
 int attn_decode_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d);
 size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits);
@@ -177,7 +177,10 @@ attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* 
  *            pages may hold anything.  max_seq_len (host) must be at least
  *            every seq_lens entry; it sizes the split plan and the
  *            workspace, attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len,
- *            d, num_splits).  A stream with no keys gets O = 0, LSE = -inf.
+ *            d, num_splits), which also covers this entry point's
+ *            automatic plan: attn_decode_splitkv's, but at least 2 chunks
+ *            from max_seq_len >= 2048 on (unequal lengths unbalance whole-
+ *            length chunks).  A stream with no keys gets O = 0, LSE = -inf.
  *   Other    q, o bf16 [B, Hq, 1, d]; lse fp32 [B, Hq] (may be NULL);
  *            max_pages * page_size <= ATTN_MAX_SEQ; every other rule as
  *            attn_decode_splitkv.
