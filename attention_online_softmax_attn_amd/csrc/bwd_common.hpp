@@ -12,21 +12,22 @@
 // build keeps bf16 MFMA operands with fp32 accumulation and writes fp32
 // gradients.
 //
-// Three kernels, no atomics (every output element has one writer):
-//   bwd_pre   per query row: (LSE * log2 e, D_i = dO_i . O_i) into the
-//             workspace, one 8-byte record per row
-//   bwd_dkdv  workgroup = (b, kv head, 32*NW keys).  K and V fragments stay in
-//             registers; for every query head of the group and every query
-//             tile that can see the keys, Q, dO and the row records stream
-//             through a ring of LDS stages (direct-to-LDS loads, the next
-//             tile prefetched while the current one is computed).
-//             S = Q K^T and dP = dO V^T put keys on the MFMA N dimension, so
-//             P and dS come out with one key per lane and feed
-//             dV += P^T dO and dK += dS^T Q straight from registers, with dO
-//             and Q read transposed from LDS.
+// Two kernels, no atomics (every output element has one writer):
 //   bwd_dq    workgroup = (b, query head, 32*NW queries), the forward's
 //             layout: S^T = K Q^T and dP^T = V dO^T keep one query per lane;
-//             dQ^T += K^T dS^T reads K transposed from LDS.
+//             dQ^T += K^T dS^T reads K transposed from LDS.  It first forms
+//             each of its rows' record (LSE * log2 e, D_i = dO_i . O_i) from
+//             the fragments it loads anyway, uses it, and stores it in the
+//             workspace (one 8-byte record per row) for:
+//   bwd_dkdv  workgroup = (b, kv head, 32*NW keys), launched after bwd_dq.
+//             K and V fragments stay in registers; for every query head of
+//             the group and every query tile that can see the keys, Q, dO and
+//             the row records stream through a ring of LDS stages
+//             (direct-to-LDS loads, the next tile prefetched while the
+//             current one is computed).  S = Q K^T and dP = dO V^T put keys on
+//             the MFMA N dimension, so P and dS come out with one key per lane
+//             and feed dV += P^T dO and dK += dS^T Q straight from registers,
+//             with dO and Q read transposed from LDS.
 //
 // The dK/dV kernel runs one wave per SIMD (its K, V fragments and dK, dV
 // accumulators exceed half the register file), so its softmax-gradient VALU

@@ -1,6 +1,7 @@
-// Backward kernels of softmax attention on gfx950, part 2: dQ (the formulas
-// and the kernel split are stated in bwd_common.hpp).  Built with the default
-// machine scheduler; the dK/dV file uses the ILP-maximising one.
+// Backward kernels of softmax attention on gfx950, part 2: dQ and the row
+// records (the formulas and the kernel split are stated in bwd_common.hpp).
+// Built with the default machine scheduler; the dK/dV file uses the
+// ILP-maximising one.
 #include <type_traits>
 
 #include "bwd_common.hpp"
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
   const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_row0 * D, (uint32_t)a.Nq * D * 2);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + q_row0 * D, (uint32_t)a.Nq * D * 2);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + q_row0 * D, (uint32_t)a.Nq * D * 2);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)a.Nk * D * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)a.Nk * D * 2);
 
@@ -80,9 +82,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     df[s] = __builtin_bit_cast(bf16x8, buf_load16(rd, src));
   }
   const bool q_in = qi < a.Nq;
-  const size_t rec = ((size_t)b * a.Hq + hq) * (size_t)a.nq_pad + qi;
-  const float l2q = q_in ? a.stats[2 * rec] : 0.0f;
-  const float ddq = q_in ? a.stats[2 * rec + 1] : 0.0f;
+  // this row's record: LSE in log2 units (+inf for a row with no visible
+  // key, so that all its P are 0) and D = dO . O, each lane summing its half
+  // of the row and its partner lane the other.  Used here, and stored for the
+  // dK/dV kernel, which runs after this one.
+  float dpart = 0.0f;
+#pragma unroll
+  for (int s = 0; s < D / 16; s++) {
+    const uint32_t src = (uint32_t)((qi * D + 16 * s + 8 * h32) * 2);
+    const bf16x8 ov = __builtin_bit_cast(bf16x8, buf_load16(ro, src));
+#pragma unroll
+    for (int e = 0; e < 8; e++) dpart = __builtin_fmaf((float)df[s][e], (float)ov[e], dpart);
+  }
+  const float dsum = halves_sum(dpart);
+  const float lse_q = q_in ? a.lse[q_row0 + qi] : 0.0f;
+  const float l2q = (lse_q == kNegInf) ? __builtin_inff() : lse_q * kLog2e;
+  const float ddq = q_in ? dsum : 0.0f;
+  if (q_in && h32 == 0) {
+    const size_t rec = ((size_t)b * a.Hq + hq) * (size_t)a.nq_pad + qi;
+    a.stats[2 * rec] = l2q;
+    a.stats[2 * rec + 1] = ddq;
+  }
 
   // lane-constant LDS offsets: rows l32, chunk 2s + h of a K (or V) tile for
   // the A operands of S^T and dP^T; transposed K reads for the A operand of

@@ -1,5 +1,5 @@
-// Backward kernels of softmax attention on gfx950, part 1: the per-row
-// records and dK, dV (the formulas and the kernel split are stated in
+// Backward kernels of softmax attention on gfx950, part 1: dK, dV and the
+// backward's launch sequence (the formulas and the kernel split are stated in
 // bwd_common.hpp).
 #include <type_traits>
 
@@ -10,33 +10,6 @@ namespace attn {
 namespace {
 
 using bwd::BwdArgs;
-
-// Row record: (LSE in log2 units, D_i).  A row with no visible key has
-// LSE = -inf; its record holds +inf so that every P of the row is 0.
-// 16 lanes per row, D/16 elements per lane.  Records of padding rows
-// (Nq <= i < nq_pad) are never written and never used unmasked.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int EPL = D / 16;
-  const int rows = a.B * a.Hq * a.Nq;
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float s = 0.0f;
-  if (row < rows) {
-    const __bf16* o = a.o + (size_t)row * D + sub * EPL;
-    const __bf16* g = a.dout + (size_t)row * D + sub * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; e++) s += (float)o[e] * (float)g[e];
-  }
-#pragma unroll
-  for (int w = 8; w >= 1; w >>= 1) s += __shfl_xor(s, w, 16);
-  if (row < rows && sub == 0) {
-    const float l = a.lse[row];
-    const size_t rec = (size_t)(row / a.Nq) * a.nq_pad + row % a.Nq;
-    a.stats[2 * rec + 0] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
-    a.stats[2 * rec + 1] = s;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK, dV.  Each wave owns 32 keys; a query tile of BQ rows is processed in
@@ -353,10 +326,10 @@ hipError_t launch(const BwdProblem& p, hipStream_t s) {
   a.g = a.Hq / a.Hkv;
   a.c = p.scale * kLog2e;
   a.scale = p.scale;
+  // dQ first: it also writes the row records the dK/dV kernel reads
   const int rows = a.B * a.Hq * a.Nq;
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + 15) / 16), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e = bwd::launch_dq(a, D, CAUSAL, s);
     if (e != hipSuccess) return e;
   }
   if (a.Nk > 0) {
@@ -364,10 +337,8 @@ hipError_t launch(const BwdProblem& p, hipStream_t s) {
     kv.n_tiles = (a.Nk + NW * 32 - 1) / (NW * 32);
     kv.n_wgs = a.B * a.Hkv * kv.n_tiles;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, ATTN_BWD_BQ, CAUSAL>), dim3(kv.n_wgs), dim3(NW * 64), 0, s, kv);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
-  if (rows > 0) return bwd::launch_dq(a, D, CAUSAL, s);
   return hipSuccess;
 }
 
