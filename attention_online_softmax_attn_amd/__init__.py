@@ -11,6 +11,7 @@ not built, or a tensor is not on the GPU, these functions raise.
     attn_decode_splitkv_fused(q, k, v, scale, num_splits=0)  -> (o, lse)
     attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, ...) -> (o, lse)
     attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len) -> (o, lse)
+    attn_fwd_varlen_paged(q, k_cache, v_cache, block_table, cu_q, seq_lens_k, max_q, max_k, ...) -> (o, lse)
     attn_bwd(q, k, v, o, dout, lse, causal, scale)    -> (dq, dk, dv)
 
 Layouts are [B, H, N, d] contiguous (q/o/dout/dq with Hq heads, k/v/dk/dv with
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_fused_workspace_bytes.restype = sz
     L.attn_decode_splitkv_fused.argtypes = L.attn_decode_splitkv.argtypes
     L.attn_decode_splitkv_fused.restype = ci
+    L.attn_fwd_varlen_paged.argtypes = [vp] * 8 + [i64] * 10 + [f32, ci, vp]
+    L.attn_fwd_varlen_paged.restype = ci
     L.attn_decode_paged.argtypes = [vp] * 7 + [i64] * 8 + [f32, ci, vp, sz, vp]
     L.attn_decode_paged.restype = ci
     L.attn_decode_splitkv_fp8.argtypes = [vp] * 7 + [i64] * 6 + [f32, ci, vp, sz, vp]
@@ -262,6 +265,42 @@ def attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, scale=None, num_splits:
                                        int(num_splits), _ptr(workspace), ws_bytes, _stream())
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_splitkv_fp8")
+    return o, (lse if want_lse else None)
+
+
+def attn_fwd_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q: int,
+                          max_seqlen_k: int, causal: bool = True, scale=None, out=None, lse=None,
+                          want_lse: bool = True):
+    """Packed variable-length forward over a paged bf16 K/V cache.  q [Hq,
+    total_q, d] packed; k_cache, v_cache [num_pages, Hkv, page_size, d];
+    block_table int32 [n_seqs, max_pages]; cu_seqlens_q int32 [n_seqs + 1];
+    seq_lens_k int32 [n_seqs].  Returns (o [Hq, total_q, d], lse [Hq, total_q])."""
+    _check_dev(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, out, lse)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape or block_table.dim() != 2:
+        raise ValueError("q must be [Hq, total_q, d], the caches [num_pages, Hkv, page_size, d], "
+                         "block_table [n_seqs, max_pages]")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("q, k_cache and v_cache must be bfloat16")
+    for t in (block_table, cu_seqlens_q, seq_lens_k):
+        if t.dtype != torch.int32:
+            raise TypeError("block_table, cu_seqlens_q and seq_lens_k must be int32")
+    Hq, total_q, d = q.shape
+    num_pages, Hkv, page, _ = k_cache.shape
+    n = seq_lens_k.numel()
+    if cu_seqlens_q.numel() != n + 1 or block_table.shape[0] != n or k_cache.shape[3] != d:
+        raise ValueError("n_seqs + 1 query offsets, n_seqs key lengths and block-table rows expected")
+    for t in (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_varlen_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(o),
+                                     _ptr(lse) if want_lse else None, _ptr(cu_seqlens_q), _ptr(seq_lens_k), n,
+                                     total_q, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d, num_pages, page,
+                                     block_table.shape[1], _scale(scale, d), int(bool(causal)), _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_varlen_paged")
     return o, (lse if want_lse else None)
 
 

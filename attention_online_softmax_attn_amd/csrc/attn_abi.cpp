@@ -150,6 +150,38 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
   return attn::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_fwd_varlen_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                  void* o, float* lse, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                  int64_t n_seqs, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                                  int64_t Hq, int64_t Hkv, int64_t d, int64_t num_pages, int64_t page_size,
+                                  int64_t max_pages, float scale, int causal, void* stream) {
+  if (n_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_pages < 0 || page_size < 0 ||
+      max_pages < 0)
+    return ATTN_ERR_INVALID;
+  attn_status st = check_common(n_seqs, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, scale, ATTN_BF16);
+  if (st != ATTN_OK) return st;
+  if (total_q > ATTN_MAX_SEQ) return ATTN_ERR_UNSUPPORTED;
+  if (page_size == 0 || page_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (max_pages > ATTN_MAX_SEQ / page_size) return ATTN_ERR_UNSUPPORTED;
+  if (n_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_OK;
+  if (!q || !o || !cu_seqlens_q || !seq_lens_k) return ATTN_ERR_INVALID;
+  if (max_seqlen_k > 0 && (!k_cache || !v_cache || !block_table || num_pages == 0 || max_pages == 0))
+    return ATTN_ERR_INVALID;
+  attn::FwdProblem p{q, k_cache, v_cache, o, lse, n_seqs, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, scale,
+                     causal ? 1 : 0, true};
+  p.cu_q = cu_seqlens_q;
+  p.tot_q = total_q;
+  p.paged = true;
+  // with max_seqlen_k = 0 every sequence is clamped to no keys and neither
+  // the table nor the cache is read
+  p.block_table = block_table;
+  p.seq_lens_k = seq_lens_k;
+  p.page = page_size;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  return attn::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_decode_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d) {
   if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128)) return -1;
   return plan_splits(B, Hkv, Nk, d, 0, false, false).splits;

@@ -51,9 +51,15 @@ struct FwdArgs {
   const int* cu_q;
   const int* cu_k;
   int tot_q, tot_k;
+  // paged K, V (with cu_q): [num_pages, Hkv, page, D]; key j of sequence b
+  // is slot j % page of page block_table[b][j / page]; sequence b has
+  // seq_lens_k[b] keys (cu_k unused)
+  const int* block_table;
+  const int* seq_lens_k;
+  int page, max_pages, num_pages;
 };
 
-template <int D, int NW, int BN, bool CAUSAL>
+template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int TILE_BYTES = BN * D * 2;       // one K or V tile
@@ -105,12 +111,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     // clamped, so that offsets that do not describe a packed batch cannot
     // take a load outside q, k or v
     const int q1 = min(a.cu_q[b + 1], a.tot_q), q0 = max(0, min(a.cu_q[b], q1));
-    const int k1 = min(a.cu_k[b + 1], a.tot_k), k0 = max(0, min(a.cu_k[b], k1));
     Nq = q1 - q0;
-    Nk = k1 - k0;
     q_head = ((size_t)hq * a.tot_q + q0) * D;
-    kv_head = ((size_t)kvh * a.tot_k + k0) * D;
     lse_row = (size_t)hq * a.tot_q + q0;
+    if constexpr (PAGED) {
+      Nk = min(max(a.seq_lens_k[b], 0), min(a.Nk, a.max_pages * a.page));
+      kv_head = 0;
+    } else {
+      const int k1 = min(a.cu_k[b + 1], a.tot_k), k0 = max(0, min(a.cu_k[b], k1));
+      Nk = k1 - k0;
+      kv_head = ((size_t)kvh * a.tot_k + k0) * D;
+    }
   } else {
     q_head = ((size_t)b * a.Hq + hq) * (size_t)Nq * D;
     kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)Nk * D;
@@ -130,18 +141,41 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   }
   const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
+  // paged: the page ids of the first 64 pages, one per lane, loaded once so
+  // that a tile's address needs no memory round trip
+  int pg_lane = 0;
+  if constexpr (PAGED) {
+    if (lane < (kend + a.page - 1) / a.page) pg_lane = a.block_table[(size_t)b * a.max_pages + lane];
+  }
+
   // ---- issue the direct-to-LDS loads of tile t into the K/V buffers kt, vt
   auto issue = [&](int t, char* kt, char* vt) {
     const int j0 = t * BN;
+    __amdgpu_buffer_rsrc_t tk = rk, tv = rv;
+    int row0 = j0;
+    if constexpr (PAGED) {
+      // a tile lies in one page (page is a multiple of BN); rows past the
+      // sequence's keys read as zeros, and a page id outside the cache is
+      // clamped into it
+      const int pi = j0 / a.page;
+      const int id = pi < 64 ? __builtin_amdgcn_readlane(pg_lane, pi)
+                             : a.block_table[(size_t)b * a.max_pages + pi];
+      const int pg = min(max(id, 0), a.num_pages - 1);
+      const size_t base = (((size_t)pg * a.Hkv + kvh) * a.page + (j0 % a.page)) * D;
+      const uint32_t bytes = (uint32_t)min(BN, Nk - j0) * D * 2;
+      tk = make_rsrc(a.k + base, bytes);
+      tv = make_rsrc(a.v + base, bytes);
+      row0 = 0;
+    }
 #pragma unroll
     for (int n = 0; n < LOADS; n++) {
       const int slab = n * NW + wave;  // 64 consecutive 16-byte LDS chunks
       const int p = slab * 64 + lane;
       const int r = p / CPR;
       const int c = (p % CPR) ^ swz<D>(r);
-      const uint32_t src = (uint32_t)(((j0 + r) * D + c * 8) * 2);
-      buf_load_lds16(rk, src, (lds_void*)(kt + slab * 1024));
-      buf_load_lds16(rv, src, (lds_void*)(vt + slab * 1024));
+      const uint32_t src = (uint32_t)(((row0 + r) * D + c * 8) * 2);
+      buf_load_lds16(tk, src, (lds_void*)(kt + slab * 1024));
+      buf_load_lds16(tv, src, (lds_void*)(vt + slab * 1024));
     }
   };
 
@@ -443,7 +477,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgsF32 a) {
   }
 }
 
-template <int D, int NW, int BN, bool CAUSAL>
+template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 hipError_t launch_bf16(const FwdProblem& p, hipStream_t s) {
   FwdArgs a;
   a.q = (const __bf16*)p.q;
@@ -464,7 +498,12 @@ hipError_t launch_bf16(const FwdProblem& p, hipStream_t s) {
   a.cu_k = p.cu_k;
   a.tot_q = (int)p.tot_q;
   a.tot_k = (int)p.tot_k;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, CAUSAL>), dim3(a.n_wgs), dim3(NW * 64), 0, s, a);
+  a.block_table = p.block_table;
+  a.seq_lens_k = p.seq_lens_k;
+  a.page = (int)p.page;
+  a.max_pages = (int)p.max_pages;
+  a.num_pages = (int)p.num_pages;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, CAUSAL, PAGED>), dim3(a.n_wgs), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -500,6 +539,18 @@ hipError_t launch_f32(const FwdProblem& p, hipStream_t s) {
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
   const bool causal = p.causal != 0;
+  if (p.paged) {
+    // packed batch over a paged K/V cache (bf16)
+    constexpr int NWB = ATTN_FWD_BIG_NW, BNB = ATTN_FWD_BIG_BN;
+    const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= 8 * 256;
+    if (p.d == 128) {
+      if (big)
+        return causal ? launch_bf16<128, NWB, BNB, true, true>(p, s) : launch_bf16<128, NWB, BNB, false, true>(p, s);
+      return causal ? launch_bf16<128, 4, 64, true, true>(p, s) : launch_bf16<128, 4, 64, false, true>(p, s);
+    }
+    if (big) return causal ? launch_bf16<64, NWB, BNB, true, true>(p, s) : launch_bf16<64, NWB, BNB, false, true>(p, s);
+    return causal ? launch_bf16<64, 4, 64, true, true>(p, s) : launch_bf16<64, 4, 64, false, true>(p, s);
+  }
   if (p.bf16) {
     // Large problems: 8 waves (256 query rows) per workgroup, which share
     // each K/V tile (half the tile loads and barriers per query row of the

@@ -26,6 +26,14 @@ struct FwdProblem {
   const int32_t* cu_q = nullptr;
   const int32_t* cu_k = nullptr;
   int64_t tot_q = 0, tot_k = 0;
+  // packed batch over a paged K/V cache (with cu_q; cu_k unused): k, v are
+  // [num_pages, Hkv, page, d] with page a multiple of 64; block_table
+  // [B, max_pages] int32; seq_lens_k [B] int32 keys per sequence; Nk is the
+  // longest
+  bool paged = false;
+  const int32_t* block_table = nullptr;
+  const int32_t* seq_lens_k = nullptr;
+  int64_t page = 0, max_pages = 0, num_pages = 0;
 };
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
 

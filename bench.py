@@ -22,7 +22,9 @@ packed batch of 16 sequences (attn_fwd_varlen); decode_fp8 = the decode shape
 over an FP8 E4M3 KV cache (attn_decode_splitkv_fp8); decode_fused = the decode
 shape in one launch (attn_decode_splitkv_fused, the last split merges);
 decode_paged = 48 streams of 512..4096 keys each (seeded) in a paged cache of
-64-key pages through a block table (attn_decode_paged).
+64-key pages through a block table (attn_decode_paged); varlen_paged = the
+varlen batch with each sequence's keys in 64-key pages of a shuffled cache
+(attn_fwd_varlen_paged).
 
 --sweep times every point the targets are stated for instead (forward causal
 N = 2048..44032 at 32 q / 8 kv heads and at B=4 H=16 N=2048, the backward, and
@@ -31,7 +33,7 @@ one JSON line per point with median / p10 / p90 / min over >= 50 calls, inputs
 rotating over copies of >= 512 MiB so that no call finds them in the MALL.
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu]
-                       [--paths fwd,decode,bwd[,varlen][,decode_fp8][,decode_fused][,decode_paged]]
+                       [--paths fwd,decode,bwd[,varlen][,decode_fp8][,decode_fused][,decode_paged][,varlen_paged]]
        python bench.py --sweep
 """
 from __future__ import annotations
@@ -168,6 +170,16 @@ def setup(paths):
         st["decode_paged"] = (to_dev(q), to_dev(kc), to_dev(vc), torch.from_numpy(table).cuda(),
                               torch.from_numpy(lens_a).cuda(), int(lens_a.max()))
         st["decode_paged_lens"] = [int(x) for x in lens_a]
+    if "varlen_paged" in paths:
+        import torch
+
+        c = VARLEN
+        lens_q, lens_k = synth.chunked_prefill_lengths(c["len_seed"], c["n"], c["lq"], c["hist"])
+        q, kc, vc, table, cu_q, lens, _ = synth.paged_varlen_inputs(c["seed"], lens_q, lens_k, c["Hq"], c["Hkv"],
+                                                                    PAGED["page"], c["d"])
+        st["varlen_paged_lens"] = (lens_q, lens_k)
+        st["varlen_paged"] = (to_dev(q), to_dev(kc), to_dev(vc), torch.from_numpy(table).cuda(),
+                              torch.from_numpy(cu_q).cuda(), torch.from_numpy(lens).cuda(), max(lens_q), max(lens_k))
     if "varlen" in paths:
         import torch
 
@@ -227,6 +239,9 @@ def run_gpu(paths, steps, warmup):
     if "varlen" in paths:
         q = st["varlen"][0]
         dev_out["varlen"] = (torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda"))
+    if "varlen_paged" in paths:
+        q = st["varlen_paged"][0]
+        dev_out["varlen_paged"] = (torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
 
     def run_path(name):
@@ -254,12 +269,17 @@ def run_gpu(paths, steps, warmup):
             q, k, v, cq, ck, mq = st["varlen"]
             o, lse = dev_out["varlen"]
             am.attn_fwd_varlen(q, k, v, cq, ck, mq, causal=True, out=o, lse=lse)
+        elif name == "varlen_paged":
+            q, kc, vc, bt, cq, lk, mq, mk = st["varlen_paged"]
+            o, lse = dev_out["varlen_paged"]
+            am.attn_fwd_varlen_paged(q, kc, vc, bt, cq, lk, mq, mk, causal=True, out=o, lse=lse)
         else:
             q, k, v, do = st["bwd"]
             o, lse, dq, dk, dv, ws = dev_out["bwd"]
             am.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
 
-    order = [p for p in ("fwd", "decode", "bwd", "decode_fp8", "decode_fused", "decode_paged", "varlen") if p in paths]
+    order = [p for p in ("fwd", "decode", "bwd", "decode_fp8", "decode_fused", "decode_paged", "varlen", "varlen_paged")
+             if p in paths]
     for _ in range(warmup):
         for p in order:
             run_path(p)
@@ -569,6 +589,17 @@ def main():
             "frac_mfma": round(f / t / 1e9 / PEAK_BF16_TFLOPS, 4),
             "shape": f"{c['n']} sequences, new tokens {sum(lens_q)}, keys {sum(lens_k)}, Hq=32 Hkv=8 d=128, "
                      "causal per sequence"}
+        total_flops += f
+    if "varlen_paged" in paths:
+        c = VARLEN
+        lens_q, lens_k = st["varlen_paged_lens"]
+        f = varlen_flops(lens_q, lens_k, c["Hq"], c["d"])
+        t = sum(per["varlen_paged"]) / len(per["varlen_paged"])
+        out_paths["varlen_paged_chunked_prefill"] = {
+            "ms": round(t, 4), "ms_median": round(med(per["varlen_paged"]), 4), "tflops": round(f / t / 1e9, 2),
+            "frac_mfma": round(f / t / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "shape": f"{c['n']} sequences, new tokens {sum(lens_q)}, keys {sum(lens_k)} in 64-key pages, "
+                     "Hq=32 Hkv=8 d=128, causal per sequence"}
         total_flops += f
     ms_step = sum(step_ms) / len(step_ms)
     value = total_flops / ms_step / 1e9

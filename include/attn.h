@@ -102,6 +102,34 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             int64_t d, float scale, int causal, attn_dtype dtype, void* stream);
 
 /*
+ * Packed variable-length forward over a paged K/V cache: attn_fwd_varlen's
+ * queries (q, o packed [Hq, total_q, d]; lse [Hq, total_q], may be NULL;
+ * cu_seqlens_q as there) against keys held in pages as serving engines keep
+ * their cache, e.g. a chunked prefill whose new tokens' K and V have been
+ * appended to the cache.  "Tang Project Derives GPU Kernels via IR ..."
+ * (section "Details") measures the engine on a long prefill and on decode at
+ * many concurrent streams of unequal length.
+ *   Cache    k_cache, v_cache: bf16 [num_pages, Hkv, page_size, d];
+ *            page_size a multiple of 64 (ATTN_ERR_UNSUPPORTED otherwise).
+ *   Table    block_table: device int32 [n_seqs, max_pages]; key j of
+ *            sequence s is slot j % page_size of page block_table[s *
+ *            max_pages + j / page_size]; page ids outside [0, num_pages) are
+ *            clamped into it (no access leaves the cache).
+ *   Keys     seq_lens_k: device int32 [n_seqs], clamped to [0,
+ *            min(max_seqlen_k, max_pages * page_size)]; keys past a
+ *            sequence's length are never read.  Causal is bottom-right per
+ *            sequence, as in attn_fwd_varlen.
+ *   Sizes    max_seqlen_q must be at least every sequence's query length;
+ *            max_seqlen_k at least every seq_lens_k entry; max_pages *
+ *            page_size <= ATTN_MAX_SEQ; ATTN_BF16 only.
+ */
+attn_status attn_fwd_varlen_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                  void* o, float* lse, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                  int64_t n_seqs, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                                  int64_t Hq, int64_t Hkv, int64_t d, int64_t num_pages, int64_t page_size,
+                                  int64_t max_pages, float scale, int causal, void* stream);
+
+/*
  * Split-KV decode: one query token per stream (Nq must be 1) against a KV
  * history of Nk keys.  Each kv head's keys are cut into num_splits chunks
  * (0 = automatic plan); every chunk yields a partial state (m, l, acc) for the

@@ -236,6 +236,26 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float):
     return o, lse
 
 
+def fwd_varlen_paged(q, k_cache, v_cache, block_table, cu_q, lens_k, scale: float, causal: bool):
+    """Packed variable-length forward with the keys of sequence s in pages:
+    key j in slot j % P of page block_table[s, j // P] of a [num_pages, Hkv,
+    P, d] cache.  Each sequence's keys are gathered into a packed [Hkv,
+    sum(lens_k), d] history and fwd_varlen above solves the batch.  Returns
+    (O [Hq, total_q, d], LSE [Hq, total_q])."""
+    kc, vc = np.asarray(k_cache), np.asarray(v_cache)
+    bt = np.asarray(block_table)
+    P = kc.shape[2]
+    ks, vs = [], []
+    for s_, L in enumerate(np.asarray(lens_k)):
+        j = np.arange(max(int(L), 0))
+        ks.append(kc[bt[s_, j // P], :, j % P, :].transpose(1, 0, 2))  # [Hkv, L, d]
+        vs.append(vc[bt[s_, j // P], :, j % P, :].transpose(1, 0, 2))
+    k = np.ascontiguousarray(np.concatenate(ks, axis=1))
+    v = np.ascontiguousarray(np.concatenate(vs, axis=1))
+    cu_k = np.concatenate([[0], np.cumsum(np.maximum(np.asarray(lens_k, np.int64), 0))]).astype(np.int32)
+    return fwd_varlen(q, k, v, cu_q, cu_k, scale, causal)
+
+
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel regions use."""
     return int(lib().oracle_num_threads())

@@ -169,3 +169,13 @@ def paged_kv_inputs(seed: int, lens, Hq: int, Hkv: int, page: int, d: int, spare
             used[perm[at + j], :min(page, n - j * page)] = True
         at += m
     return q, kc, vc, table, np.asarray(lens, np.int32), used
+
+
+def paged_varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, page: int, d: int, spare_pages: int = 3):
+    """Packed queries q [Hq, sum(lens_q), d] (bf16-exact) with int32 offsets
+    cu_q, and a paged cache as paged_kv_inputs gives it for lens_k (K, V
+    [num_pages, Hkv, page, d], block table, int32 lengths, used slots)."""
+    _, kc, vc, table, lens, used = paged_kv_inputs(seed, lens_k, Hq, Hkv, page, d, spare_pages)
+    cu_q = offsets(lens_q)
+    (q,) = normal(seed + 104729, [(Hq, int(cu_q[-1]), d)], True)
+    return q, kc, vc, table, cu_q, lens, used

@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_varlen", "attn_decode_splitkv", "attn_decode_splitkv_fp8", "attn_bwd",
               "attn_decode_splitkv_fused", "attn_decode_fused_workspace_bytes", "attn_decode_workspace_bytes",
-              "attn_decode_paged",
+              "attn_decode_paged", "attn_fwd_varlen_paged",
               "attn_bwd_workspace_bytes", "attn_decode_num_splits", "attn_strerror"):
         assert n in names
 
@@ -202,6 +202,42 @@ def test_decode_fused_workspace_layout():
             assert one == 0                       # one chunk: no partials, no counts
         else:
             assert one == two + 65536                # a fixed region of arrival counts first
+
+
+def fvp(q=P, k=P, v=P, bt=P, o=P, lse=P, cq=P, lk=P, n=4, tq=1000, maxq=400, maxk=2000, Hq=32, Hkv=8, d=128,
+        pages=200, page=64, maxp=40, scale=0.088, causal=1):
+    return am.lib().attn_fwd_varlen_paged(q, k, v, bt, o, lse, cq, lk, n, tq, maxq, maxk, Hq, Hkv, d, pages, page,
+                                          maxp, scale, causal, None)
+
+
+@no_gpu
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(page=32), am.ATTN_ERR_UNSUPPORTED),                   # not a multiple of 64
+        (dict(page=0), am.ATTN_ERR_UNSUPPORTED),
+        (dict(maxp=(1 << 22) // 64 + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(maxk=(1 << 22) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(tq=(1 << 22) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(n=-1), am.ATTN_ERR_INVALID),
+        (dict(cq=NUL), am.ATTN_ERR_INVALID),
+        (dict(lk=NUL), am.ATTN_ERR_INVALID),
+        (dict(bt=NUL), am.ATTN_ERR_INVALID),
+        (dict(k=NUL), am.ATTN_ERR_INVALID),
+        (dict(pages=0), am.ATTN_ERR_INVALID),
+        (dict(Hq=30), am.ATTN_ERR_INVALID),
+        (dict(d=80), am.ATTN_ERR_UNSUPPORTED),
+        (dict(scale=float("nan")), am.ATTN_ERR_INVALID),
+    ],
+)
+def test_fwd_varlen_paged_rejects(kw, code):
+    assert fvp(**kw) == code
+
+
+@no_gpu
+def test_fwd_varlen_paged_empty_launches_nothing():
+    assert fvp(q=NUL, k=NUL, v=NUL, bt=NUL, o=NUL, lse=NUL, cq=NUL, lk=NUL, n=0) == am.ATTN_OK
+    assert fvp(q=NUL, k=NUL, v=NUL, bt=NUL, o=NUL, lse=NUL, cq=NUL, lk=NUL, tq=0) == am.ATTN_OK
 
 
 def decp(q=P, k=P, v=P, bt=P, sl=P, o=P, lse=P, B=4, Hq=32, Hkv=8, d=128, pages=100, page=64, maxp=20,
