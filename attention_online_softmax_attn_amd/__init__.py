@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, vp, sz, ci, vp]
     L.attn_bwd.restype = ci
+    L.attn_bwd_bf16_grads.argtypes = L.attn_bwd.argtypes
+    L.attn_bwd_bf16_grads.restype = ci
     L.attn_strerror.argtypes = [ci]
     L.attn_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -344,21 +346,31 @@ def bwd_workspace_bytes(B: int, Hq: int, Nq: int, d: int) -> int:
     return int(lib().attn_bwd_workspace_bytes(B, Hq, Nq, d))
 
 
-def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale=None, workspace=None, dq=None, dk=None, dv=None):
-    """Backward from the saved LSE.  Returns fp32 (dq, dk, dv)."""
+def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale=None, workspace=None, dq=None, dk=None, dv=None,
+             grad_dtype=None):
+    """Backward from the saved LSE.  Returns (dq, dk, dv) in grad_dtype:
+    torch.float32 (the default) or torch.bfloat16 (attn_bwd_bf16_grads: the
+    fp32 results rounded to nearest even)."""
+    gdt = torch.float32 if grad_dtype is None else grad_dtype
+    if gdt not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"attn_bwd: grad_dtype must be float32 or bfloat16, not {gdt}")
     _check_dev(q, k, v, o, dout, lse, workspace, dq, dk, dv)
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
-    f32 = dict(dtype=torch.float32, device=q.device)
-    dq = torch.empty(q.shape, **f32) if dq is None else dq
-    dk = torch.empty(k.shape, **f32) if dk is None else dk
-    dv = torch.empty(v.shape, **f32) if dv is None else dv
+    for g in (dq, dk, dv):
+        if g is not None and g.dtype != gdt:
+            raise ValueError(f"attn_bwd: gradient buffers must be {gdt}")
+    gd = dict(dtype=gdt, device=q.device)
+    dq = torch.empty(q.shape, **gd) if dq is None else dq
+    dk = torch.empty(k.shape, **gd) if dk is None else dk
+    dv = torch.empty(v.shape, **gd) if dv is None else dv
     need = bwd_workspace_bytes(B, Hq, Nq, d)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B,
-                        Hq, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _ptr(workspace), ws_bytes,
-                        _dtype_code(q), _stream())
+    fn = lib().attn_bwd if gdt == torch.float32 else lib().attn_bwd_bf16_grads
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B,
+            Hq, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _ptr(workspace), ws_bytes,
+            _dtype_code(q), _stream())
     if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd" if gdt == torch.float32 else "attn_bwd_bf16_grads")
     return dq, dk, dv

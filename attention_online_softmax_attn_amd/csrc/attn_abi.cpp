@@ -365,10 +365,12 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d) {
   return align256((size_t)B * Hq * attn::bwd_record_rows(Nq) * 2 * sizeof(float));
 }
 
-attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                     float* dq, float* dk, float* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-                     int64_t d, float scale, int causal, void* workspace, size_t workspace_bytes, attn_dtype dtype,
-                     void* stream) {
+}  // extern "C"
+
+static attn_status bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int grad_bf16, int64_t B, int64_t Hq,
+                              int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                              void* workspace, size_t workspace_bytes, attn_dtype dtype, void* stream) {
   attn_status st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
@@ -396,7 +398,26 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   p.d = d;
   p.scale = scale;
   p.causal = causal ? 1 : 0;
+  p.grad_bf16 = grad_bf16;
   return attn::launch_bwd(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" {
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     float* dq, float* dk, float* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                     int64_t d, float scale, int causal, void* workspace, size_t workspace_bytes, attn_dtype dtype,
+                     void* stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, 0, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace,
+                    workspace_bytes, dtype, stream);
+}
+
+attn_status attn_bwd_bf16_grads(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                                int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, void* workspace,
+                                size_t workspace_bytes, attn_dtype dtype, void* stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace,
+                    workspace_bytes, dtype, stream);
 }
 
 }  // extern "C"

@@ -77,7 +77,7 @@ struct BwdArgs {
   const __bf16* o;
   const __bf16* dout;
   const float* lse;
-  float* dq;
+  float* dq;     // fp32 gradients, or bf16 ones (the same addresses as __bf16*) when grad_bf16
   float* dk;
   float* dv;
   float* stats;  // [B, Hq, nq_pad] x (LSE * log2 e, D)
@@ -87,6 +87,7 @@ struct BwdArgs {
   int n_tiles, n_wgs;
   float c;      // scale * log2(e)
   float scale;
+  int grad_bf16;  // 1: dq, dk, dv are bf16, each the fp32 result rounded to nearest even
 };
 
 // dQ for every query row; d is 64 or 128 (bwd_dq.hip)

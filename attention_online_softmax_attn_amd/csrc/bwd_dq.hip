@@ -19,7 +19,7 @@ namespace {
 // 32-key block at a time so that fragments, accumulators and the block's
 // S^T / dP^T fit the 256 registers a wave has when two share a SIMD; the SIMD
 // then overlaps one wave's exponentials with the other's MFMAs.
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool G16>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64;
   constexpr int TILE = BN * D * 2;            // one K or V tile
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
   }
 
   if (q_in) {
-    float* row = a.dq + (q_row0 + qi) * D;
+    // lane holds dims cb*32 + 8 g4 + 4h .. +3 of row qi
 #pragma unroll
     for (int cb = 0; cb < D / 32; cb++)
 #pragma unroll
@@ -200,7 +200,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
         f32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; e++) w[e] = acc[cb][4 * g4 + e] * a.scale;
-        *(f32x4*)(row + cb * 32 + 8 * g4 + 4 * h32) = w;
+        const size_t at = (q_row0 + qi) * D + cb * 32 + 8 * g4 + 4 * h32;
+        if constexpr (G16)
+          *(bf16x4*)((__bf16*)a.dq + at) = bf16x4{to_bf16(w[0]), to_bf16(w[1]), to_bf16(w[2]), to_bf16(w[3])};
+        else
+          *(f32x4*)(a.dq + at) = w;
       }
   }
 }
@@ -210,7 +214,10 @@ hipError_t launch_nw(const BwdArgs& a, hipStream_t s) {
   BwdArgs qa = a;
   qa.n_tiles = (a.Nq + NW * 32 - 1) / (NW * 32);
   qa.n_wgs = a.B * a.Hq * qa.n_tiles;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(qa.n_wgs), dim3(NW * 64), 0, s, qa);
+  if (a.grad_bf16)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL, true>), dim3(qa.n_wgs), dim3(NW * 64), 0, s, qa);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL, false>), dim3(qa.n_wgs), dim3(NW * 64), 0, s, qa);
   return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ using bwd::BwdArgs;
 // ---------------------------------------------------------------------------
 // dK, dV.  Each wave owns 32 keys; a query tile of BQ rows is processed in
 // 32-row blocks.
-template <int D, int NW, int BQ, bool CAUSAL>
+template <int D, int NW, int BQ, bool CAUSAL, bool G16>
 __global__ __launch_bounds__(NW * 64, ATTN_BWD_KV_OCC) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int TILE = BQ * D * 2;  // bytes of one Q or dO tile
   constexpr int STAGE = 2 * TILE + 1024;  // Q, dO, row records (BQ * 8 <= 1024 bytes)
@@ -288,16 +288,20 @@ __global__ __launch_bounds__(NW * 64, ATTN_BWD_KV_OCC) void bwd_dkdv_kernel(BwdA
   }
 
   // dV, dK accumulators: lane holds dim cb*32 + l32 of keys jw + 8(r/4) + 4h + r%4
-  float* dkh = a.dk + kv_head;
-  float* dvh = a.dv + kv_head;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int j = jw + 8 * (r >> 2) + 4 * h32 + (r & 3);
     if (j < a.Nk) {
 #pragma unroll
       for (int cb = 0; cb < D / 32; cb++) {
-        dkh[(size_t)j * D + cb * 32 + l32] = dk_acc[cb][r] * a.scale;
-        dvh[(size_t)j * D + cb * 32 + l32] = dv_acc[cb][r];
+        const size_t at = kv_head + (size_t)j * D + cb * 32 + l32;
+        if constexpr (G16) {
+          ((__bf16*)a.dk)[at] = to_bf16(dk_acc[cb][r] * a.scale);
+          ((__bf16*)a.dv)[at] = to_bf16(dv_acc[cb][r]);
+        } else {
+          a.dk[at] = dk_acc[cb][r] * a.scale;
+          a.dv[at] = dv_acc[cb][r];
+        }
       }
     }
   }
@@ -313,9 +317,10 @@ hipError_t launch(const BwdProblem& p, hipStream_t s) {
   a.o = (const __bf16*)p.o;
   a.dout = (const __bf16*)p.dout;
   a.lse = p.lse;
-  a.dq = p.dq;
-  a.dk = p.dk;
-  a.dv = p.dv;
+  a.dq = (float*)p.dq;
+  a.dk = (float*)p.dk;
+  a.dv = (float*)p.dv;
+  a.grad_bf16 = p.grad_bf16;
   a.stats = p.stats;
   a.nq_pad = (int)bwd_record_rows(p.Nq);
   a.B = (int)p.B;
@@ -336,7 +341,10 @@ hipError_t launch(const BwdProblem& p, hipStream_t s) {
     BwdArgs kv = a;
     kv.n_tiles = (a.Nk + NW * 32 - 1) / (NW * 32);
     kv.n_wgs = a.B * a.Hkv * kv.n_tiles;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, ATTN_BWD_BQ, CAUSAL>), dim3(kv.n_wgs), dim3(NW * 64), 0, s, kv);
+    if (a.grad_bf16)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, ATTN_BWD_BQ, CAUSAL, true>), dim3(kv.n_wgs), dim3(NW * 64), 0, s, kv);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, ATTN_BWD_BQ, CAUSAL, false>), dim3(kv.n_wgs), dim3(NW * 64), 0, s, kv);
     return hipGetLastError();
   }
   return hipSuccess;

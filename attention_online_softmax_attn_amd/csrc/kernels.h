@@ -78,13 +78,14 @@ struct BwdProblem {
   const void* o;
   const void* dout;
   const float* lse;
-  float* dq;
-  float* dk;
-  float* dv;
+  void* dq;      // fp32, or bf16 when grad_bf16
+  void* dk;
+  void* dv;
   float* stats;  // workspace: [B, Hq, bwd_record_rows(Nq)] x 2 fp32 (LSE * log2 e, D)
   int64_t B, Hq, Hkv, Nq, Nk, d;
   float scale;
   int causal;
+  int grad_bf16;
 };
 // Rows of backward row records per head: Nq rounded up to 128.
 inline int64_t bwd_record_rows(int64_t Nq) { return (Nq + 127) / 128 * 128; }

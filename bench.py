@@ -28,7 +28,8 @@ varlen batch with each sequence's keys in 64-key pages of a shuffled cache
 
 --sweep times every point the targets are stated for instead (forward causal
 N = 2048..44032 at 32 q / 8 kv heads and at B=4 H=16 N=2048, the backward, and
-the decode at 1/16/48 streams x 512..4096 keys with both decode entry points),
+the backward also with bf16 gradients, and the decode at 1/16/48 streams x
+512..4096 keys with both decode entry points),
 one JSON line per point with median / p10 / p90 / min over >= 50 calls, inputs
 rotating over copies of >= 512 MiB so that no call finds them in the MALL.
 
@@ -465,6 +466,14 @@ def sweep():
     tf = f / t["ms_median"] / 1e9
     emit({"path": "bwd", "shape": f"B={B} H={H} N={N} d={d} causal", "copies": n, **t, "tflops": round(tf, 1),
           "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "target": 0.5, "meets": tf / PEAK_BF16_TFLOPS >= 0.5})
+    # the same backward writing bf16 gradients (attn_bwd_bf16_grads)
+    g16 = dict(dtype=torch.bfloat16, device="cuda")
+    dq, dk, dv = torch.empty(B, H, N, d, **g16), torch.empty(B, H, N, d, **g16), torch.empty(B, H, N, d, **g16)
+    t = time_calls(lambda i: am.attn_bwd(*sets[i], causal=True, workspace=ws, dq=dq, dk=dk, dv=dv,
+                                         grad_dtype=torch.bfloat16), n)
+    tf = f / t["ms_median"] / 1e9
+    emit({"path": "bwd_bf16_grads", "shape": f"B={B} H={H} N={N} d={d} causal", "copies": n, **t,
+          "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "meets": None})
     del sets, dq, dk, dv
     # decode, two launches and one
     for B, L in SWEEP_DECODE:

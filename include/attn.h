@@ -251,6 +251,22 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int64_t d, float scale, int causal, void* workspace, size_t workspace_bytes, attn_dtype dtype,
                      void* stream);
 
+/*
+ * attn_bwd with bf16 gradients: dq [B,Hq,Nq,d] and dk, dv [B,Hkv,Nk,d] are
+ * bf16, each element the fp32 value attn_bwd writes for the same arguments
+ * rounded to nearest even (the same kernels; only the final stores differ),
+ * so the gradient traffic halves for callers whose parameters are bf16.  The
+ * first page ("Não escreva kernels, derive-os", section "Aprofundamento",
+ * third paragraph) reports that its fused bf16 backward missed an fp32
+ * tolerance; here the accumulation stays fp32 and only the output is
+ * rounded, which adds at most half a bf16 ulp of each gradient (2^-9 of its
+ * magnitude).  Workspace, ownership, errors and every other rule as attn_bwd.
+ */
+attn_status attn_bwd_bf16_grads(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                                int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, void* workspace,
+                                size_t workspace_bytes, attn_dtype dtype, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* attn_strerror(attn_status status);
 

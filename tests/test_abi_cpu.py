@@ -337,18 +337,28 @@ def test_split_plan_and_workspace():
     assert am.bwd_workspace_bytes(4, 16, 2048, 128) >= 4 * 16 * 2048 * 4
 
 
-def bwd(ws=P, ws_bytes=1 << 30, dt=am.ATTN_BF16, d=128, lse=P, Hq=4, Hkv=2):
-    return am.lib().attn_bwd(P, P, P, P, P, lse, P, P, P, 1, Hq, Hkv, 64, 64, d, 0.1, 1, ws, ws_bytes, dt, None)
+def bwd(ws=P, ws_bytes=1 << 30, dt=am.ATTN_BF16, d=128, lse=P, Hq=4, Hkv=2, dq=P, fn="attn_bwd"):
+    return getattr(am.lib(), fn)(P, P, P, P, P, lse, dq, P, P, 1, Hq, Hkv, 64, 64, d, 0.1, 1, ws, ws_bytes, dt, None)
 
 
 @no_gpu
-def test_bwd_rejects():
-    assert bwd(ws=NUL) == am.ATTN_ERR_WORKSPACE
-    assert bwd(ws_bytes=4) == am.ATTN_ERR_WORKSPACE
-    assert bwd(dt=am.ATTN_F32) == am.ATTN_ERR_UNSUPPORTED
-    assert bwd(d=32) == am.ATTN_ERR_UNSUPPORTED
-    assert bwd(lse=NUL) == am.ATTN_ERR_INVALID
-    assert bwd(Hq=3) == am.ATTN_ERR_INVALID
+@pytest.mark.parametrize("fn", ["attn_bwd", "attn_bwd_bf16_grads"])
+def test_bwd_rejects(fn):
+    assert bwd(ws=NUL, fn=fn) == am.ATTN_ERR_WORKSPACE
+    assert bwd(ws_bytes=4, fn=fn) == am.ATTN_ERR_WORKSPACE
+    assert bwd(dt=am.ATTN_F32, fn=fn) == am.ATTN_ERR_UNSUPPORTED
+    assert bwd(d=32, fn=fn) == am.ATTN_ERR_UNSUPPORTED
+    assert bwd(lse=NUL, fn=fn) == am.ATTN_ERR_INVALID
+    assert bwd(dq=NUL, fn=fn) == am.ATTN_ERR_INVALID
+    assert bwd(Hq=3, fn=fn) == am.ATTN_ERR_INVALID
+
+
+def test_bwd_binding_refuses_other_gradient_dtypes():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="grad_dtype"):
+        am.attn_bwd(q, q, q, q, q, torch.zeros(1, 1, 4), grad_dtype=torch.float16)
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -105,3 +105,53 @@ def test_c5_full_size_sampled_heads(oracle_mod):
     assert np.max(np.abs(gk.sum(axis=2))) <= 0.5, np.max(np.abs(gk.sum(axis=2)))
     sdo = do.astype(np.float64).sum(axis=2)
     assert np.max(np.abs(gv.sum(axis=2) - sdo)) <= 0.5
+
+
+# ---------------------------------------------------------------- bf16 gradients (attn_bwd_bf16_grads)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 17, 17, 128), (1, 4, 2, 129, 129, 128), (1, 4, 1, 300, 300, 64),
+                                   (1, 2, 1, 260, 100, 128), (2, 8, 2, 512, 512, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_grads_are_the_fp32_grads_rounded(shape, causal):
+    # the same kernels with bf16 final stores: every element equals the fp32
+    # path's value rounded to nearest even
+    B, Hq, Hkv, Nq, Nk, d = shape
+    print(f"bf16 grads case {shape} causal={causal}", flush=True)
+    q, k, v, do = synth.attn_inputs(5600 + Nq + Nk + d, B, Hq, Hkv, Nq, Nk, d, bf16=True, with_dout=True)
+    qd, kd, vd, dod = dev(q, True), dev(k, True), dev(v, True), dev(do, True)
+    o, lse = am.attn_fwd(qd, kd, vd, causal=causal)
+    g32 = am.attn_bwd(qd, kd, vd, o, dod, lse, causal=causal)
+    g16 = am.attn_bwd(qd, kd, vd, o, dod, lse, causal=causal, grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), g32, g16):
+        assert b.dtype == torch.bfloat16
+        assert torch.equal(a.to(torch.bfloat16).view(torch.int16), b.view(torch.int16)), name
+
+
+def test_bf16_grads_c5_tolerance_study(oracle_mod):
+    # B=4 H=16 N=2048 d=128 causal, four sampled heads against the fp64
+    # oracle: rounding the output adds at most half a bf16 ulp, 2^-9 |g|, to
+    # the fp32 path's error; the bar stays the gradient tolerance
+    B, H, N, d = 4, 16, 2048, 128
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = synth.attn_inputs(5, B, H, H, N, N, d, bf16=True, with_dout=True)
+    print("C5 bwd, bf16 gradients: launching", flush=True)
+    qd, kd, vd, dod = dev(q, True), dev(k, True), dev(v, True), dev(do, True)
+    o, lse = am.attn_fwd(qd, kd, vd, causal=True, scale=scale)
+    g16 = [host(g) for g in am.attn_bwd(qd, kd, vd, o, dod, lse, causal=True, scale=scale, grad_dtype=torch.bfloat16)]
+    g32 = [host(g) for g in am.attn_bwd(qd, kd, vd, o, dod, lse, causal=True, scale=scale)]
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(50005)
+    picks = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(2)]
+    bs = [p[0] for p in picks]
+    hs = [p[1] for p in picks]
+    sl = lambda x: np.ascontiguousarray(x[bs, hs][:, None])
+    exp = oracle_mod.bwd(sl(q), sl(k), sl(v), sl(do), scale, True)
+    for name, a16, a32, e in zip(("dQ", "dK", "dV"), g16, g32, exp):
+        gmax = float(np.abs(e).max())
+        e32 = assert_close(name + " fp32", a32[bs, hs], e[:, 0], TOL_GRAD)
+        e16 = assert_close(name + " bf16", a16[bs, hs], e[:, 0], TOL_GRAD)
+        # the rounding adds no more than half an ulp at the largest magnitude
+        assert e16 <= e32 + 2.0 ** -9 * gmax * 1.0001
+        print(f"  {name}: max|g| {gmax:.3f}  err fp32 {e32:.3e}  err bf16 {e16:.3e}", flush=True)
