@@ -44,6 +44,10 @@ struct FwdArgs {
   float* lse;
   int B, Hq, Hkv, Nq, Nk, g;
   int n_qtiles, n_wgs;
+  // 1: the whole grid is resident at once, two workgroups per CU, and the
+  // XCD-local order pairs slot t of an XCD (heaviest first) with slot
+  // t + half (lightest first), so that each CU's two tiles add up evenly
+  int snake;
   float c;  // scale * log2(e)
   // packed variable-length batch (null for a dense one): sequence b holds
   // query rows [cu_q[b], cu_q[b+1]) of q, o and lse and key rows
@@ -58,6 +62,16 @@ struct FwdArgs {
   const int* seq_lens_k;
   int page, max_pages, num_pages;
 };
+
+// Launch index -> the index lpt_order ranks: within each XCD (launch index
+// mod 8) the first half of the dispatch order keeps the heaviest-first
+// ranks and the second half takes the remaining ranks lightest first.  A
+// bijection on [0, n) for n a multiple of 8.
+__device__ __forceinline__ int snake_pid(int pid, int n, int on) {
+  if (!on) return pid;
+  const int T = n / 8, half = (T + 1) / 2, x = pid % 8, t = pid / 8;
+  return x + 8 * (t < half ? t : T - 1 - (t - half));
+}
 
 template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
@@ -93,7 +107,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // more work than others: there every XCD gets a share of every sequence.
   const WorkItem wi = (a.cu_q != nullptr)
                           ? WorkItem{(int)(blockIdx.x % (a.B * a.Hkv)), (int)(blockIdx.x / (a.B * a.Hkv))}
-                          : lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_qtiles);
+                          : lpt_order(snake_pid(blockIdx.x, a.n_wgs, a.snake), a.B * a.Hkv, a.g * a.n_qtiles);
   const int pair = wi.pair;
   const int rem = wi.sub;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
@@ -493,6 +507,7 @@ hipError_t launch_bf16(const FwdProblem& p, hipStream_t s) {
   a.g = a.Hq / a.Hkv;
   a.n_qtiles = (a.Nq + NW * 32 - 1) / (NW * 32);
   a.n_wgs = a.B * a.Hq * a.n_qtiles;
+  a.snake = (CAUSAL && NW == 4 && p.cu_q == nullptr && (a.B * a.Hkv) % 8 == 0 && a.n_wgs <= 2 * 256) ? 1 : 0;
   a.c = p.scale * kLog2e;
   a.cu_q = p.cu_q;
   a.cu_k = p.cu_k;

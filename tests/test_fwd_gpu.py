@@ -151,6 +151,7 @@ MIDDLE = [
     (4, 16, 16, 2048, 2048, 128, "4-wave"),
     (2, 32, 8, 1100, 1300, 64, "4-wave"),
     (1, 32, 8, 2048, 2048, 128, "4-wave"),
+    (2, 16, 8, 2048, 2048, 128, "4-wave"),  # whole grid resident: second half of each XCD lightest first
     (1, 16, 4, 4000, 3900, 128, "4-wave"),
 ]
 
