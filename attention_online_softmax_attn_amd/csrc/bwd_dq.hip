@@ -223,8 +223,9 @@ hipError_t launch_nw(const BwdArgs& a, hipStream_t s) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
-  // 8 waves (256 rows) per workgroup when that still gives 8 workgroups per CU
-  const bool big = (int64_t)a.B * a.Hq * ((a.Nq + 255) / 256) >= 8 * 256;
+  // 8 waves (256 rows) per workgroup when that still gives two workgroups per
+  // CU over the launch (the forward's rule; ~1 % faster at 4 x 16 heads x 2048)
+  const bool big = (int64_t)a.B * a.Hq * ((a.Nq + 255) / 256) >= 2 * 256;
   return big ? launch_nw<D, CAUSAL, 8>(a, s) : launch_nw<D, CAUSAL, 4>(a, s);
 }
 

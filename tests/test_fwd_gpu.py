@@ -142,13 +142,15 @@ def test_no_writes_outside_outputs():
 
 
 # ---------------------------------------------------------------- the 4-wave configuration at scale
-# The launcher runs the 8-wave kernel for at least 2048 query tiles of 256
+# The launcher runs the 8-wave kernel for at least 512 query tiles of 256
 # rows and the 4-wave kernel below that; the small shapes above take the
-# 4-wave kernel with few workgroups, these with many (up to 1024 tiles of
-# 128 rows), ragged and with Nq != Nk, on sampled rows.
+# 4-wave kernel with few workgroups, these with many (up to 1022 tiles of
+# 128 rows), ragged and with Nq != Nk, on sampled rows, plus the 8-wave
+# kernel right at its threshold.
 MIDDLE = [
     # B, Hq, Hkv, Nq, Nk, d, expected configuration
-    (4, 16, 16, 2048, 2048, 128, "4-wave"),
+    (4, 16, 16, 2048, 2048, 128, "8-wave"),
+    (1, 31, 31, 4096, 4096, 128, "4-wave"),  # 496 tiles of 256 rows, 992 workgroups
     (2, 32, 8, 1100, 1300, 64, "4-wave"),
     (1, 32, 8, 2048, 2048, 128, "4-wave"),
     (2, 16, 8, 2048, 2048, 128, "4-wave"),  # whole grid resident: second half of each XCD lightest first
@@ -157,7 +159,7 @@ MIDDLE = [
 
 
 def _config(B, Hq, Nq):
-    return "8-wave" if B * Hq * ((Nq + 255) // 256) >= 2048 else "4-wave"
+    return "8-wave" if B * Hq * ((Nq + 255) // 256) >= 512 else "4-wave"
 
 
 @pytest.mark.parametrize("shape", MIDDLE)
@@ -179,7 +181,7 @@ def test_middle_grid_sampled_rows(oracle_mod, shape, causal):
 
 
 # ---------------------------------------------------------------- large grids (the 8-wave kernel)
-# Problems with at least 8 workgroups of 256 query rows per CU (>= 2048 of
+# Problems with at least two workgroups of 256 query rows per CU (>= 512 of
 # them) run the 8-wave kernel; these shapes reach it with ragged lengths,
 # grouped-query heads and Nq != Nk, checked on sampled rows (the oracle of a
 # whole 8k x 8k problem would take minutes on the host).
@@ -195,7 +197,7 @@ LARGE = [
 @pytest.mark.parametrize("causal", [True, False])
 def test_large_grid_sampled_rows(oracle_mod, shape, causal):
     B, Hq, Hkv, Nq, Nk, d = shape
-    assert B * Hq * ((Nq + 255) // 256) >= 8 * 256
+    assert B * Hq * ((Nq + 255) // 256) >= 2 * 256
     scale = 1.0 / math.sqrt(d)
     q, k, v = synth.attn_inputs(600 + Nq + d, B, Hq, Hkv, Nq, Nk, d, bf16=True)
     print(f"large case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal}", flush=True)
