@@ -138,8 +138,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   constexpr int CPR = D / 8;
   constexpr int LOADS = BN * CPR / 64;   // per lane per tile, one wave loads its own tile
   static_assert(BN == 32, "one 32-key MFMA block per tile");
-  // per wave: two stages; the same memory is reused for the final fold
-  __shared__ __attribute__((aligned(1024))) char smem[kWaves * 2 * STAGE];
+  // per wave: two stages.  One LDS object per stage, each holding every
+  // wave's tile of that stage, so that the compiler can tell the prefetch
+  // into one stage from the reads of the other (1-2 % faster than one array
+  // with per-wave offsets); stage 0 also holds the final fold.
+  constexpr int FOLD = kWaves * 32 * D * 4 + 2 * kWaves * 32 * 4;
+  constexpr int ST0 = kWaves * STAGE > FOLD ? kWaves * STAGE : FOLD;
+  __shared__ __attribute__((aligned(1024))) char stg0[ST0];
+  __shared__ __attribute__((aligned(1024))) char stg1[kWaves * STAGE];
+  char* const smem = stg0;
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -167,7 +174,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   const size_t q_grp = ((size_t)b * a.Hq + (size_t)kvh * a.g) * D;  // the g query rows of this kv head
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_grp, (uint32_t)a.g * D * 2);
 
-  char* wbase = smem + wave * 2 * STAGE;
+  char* const w0 = stg0 + wave * STAGE;
+  char* const w1 = stg1 + wave * STAGE;
 
   // paged: the page ids of this chunk's first 64 pages, one per lane, loaded
   // once so that a tile's address needs no memory round trip
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
     }
   };
 
-  if (my_tiles > 0) issue(0, wbase, wbase + TILE_BYTES);
+  if (my_tiles > 0) issue(0, w0, w0 + TILE_BYTES);
 
   // query fragments: column l32 is query head kvh*g + l32 (zero beyond g)
   bf16x8 qf[D / 16];
@@ -282,12 +290,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
     if (i + 1 < my_tiles) issue(i + 1, kn, vn);
     compute(i, kc, vc);
   };
-  char* const s0 = wbase;
-  char* const s1 = wbase + STAGE;
   for (int i = 0; i < my_tiles; i += 2) {
-    step(i, s0, s0 + TILE_BYTES, s1, s1 + TILE_BYTES);
+    step(i, w0, w0 + TILE_BYTES, w1, w1 + TILE_BYTES);
     if (i + 1 >= my_tiles) break;
-    step(i + 1, s1, s1 + TILE_BYTES, s0, s0 + TILE_BYTES);
+    step(i + 1, w1, w1 + TILE_BYTES, w0, w0 + TILE_BYTES);
   }
 
   // ---- fold the four wave states: the monoid rule, through LDS
