@@ -28,6 +28,8 @@ namespace attn {
 namespace {
 
 constexpr float kTau = 8.0f;
+// waves per workgroup of the FP8 decode kernel (the bf16 kernel takes 2 or 4
+// by grid size)
 #ifndef ATTN_DECODE_WAVES
 #define ATTN_DECODE_WAVES 4
 #endif
@@ -123,15 +125,15 @@ __device__ void merge_if_last(const DecArgs& a, int b, int kvh, int pair) {
   __syncthreads();
   if (s_last == 0u) return;
   const int total = a.g * D;
-  for (int e = threadIdx.x; e < total; e += kWaves * 64) {
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
     const int qh = e / D, col = e % D;
     fold_split_states<D, true>(a, (size_t)b * a.Hq + kvh * a.g + qh, col);
   }
   if (threadIdx.x == 0) atomicExch(a.counters + pair, 0u);
 }
 
-template <int D, bool PAGED>
-__global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs a) {
+template <int D, bool PAGED, int NWV>
+__global__ __launch_bounds__(NWV * 64, 1) void decode_partial_kernel(DecArgs a) {
   constexpr int BN = kDecodeTile;
   constexpr int TILE_BYTES = BN * D * 2;
   constexpr int STAGE = 2 * TILE_BYTES;  // K then V
@@ -142,10 +144,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   // wave's tile of that stage, so that the compiler can tell the prefetch
   // into one stage from the reads of the other (1-2 % faster than one array
   // with per-wave offsets); stage 0 also holds the final fold.
-  constexpr int FOLD = kWaves * 32 * D * 4 + 2 * kWaves * 32 * 4;
-  constexpr int ST0 = kWaves * STAGE > FOLD ? kWaves * STAGE : FOLD;
+  constexpr int FOLD = NWV * 32 * D * 4 + 2 * NWV * 32 * 4;
+  constexpr int ST0 = NWV * STAGE > FOLD ? NWV * STAGE : FOLD;
   __shared__ __attribute__((aligned(1024))) char stg0[ST0];
-  __shared__ __attribute__((aligned(1024))) char stg1[kWaves * STAGE];
+  __shared__ __attribute__((aligned(1024))) char stg1[NWV * STAGE];
   char* const smem = stg0;
 
   const int lane = threadIdx.x & 63;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   const int k0 = split * a.chunk;
   const int k1 = min(nk_b, k0 + a.chunk);
   const int n_tiles = k1 > k0 ? (k1 - k0 + BN - 1) / BN : 0;
-  const int my_tiles = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + NWV - 1) / NWV : 0;
 
   const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)a.Nk * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (PAGED ? 0 : kv_head), (uint32_t)a.Nk * D * 2);
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   }
 
   auto issue = [&](int i, char* kt, char* vt) {
-    const int j0 = k0 + (wave + kWaves * i) * BN;
+    const int j0 = k0 + (wave + NWV * i) * BN;
     __amdgpu_buffer_rsrc_t tk = rk, tv = rv;
     int row0 = j0;
     if constexpr (PAGED) {
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   const int swl = swz<D>(l32);
 
   auto compute = [&](int i, const char* kt, const char* vt) {
-    const int j0 = k0 + (wave + kWaves * i) * BN;
+    const int j0 = k0 + (wave + NWV * i) * BN;
     f32x16 st = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; s++) {
@@ -299,9 +301,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   // ---- fold the four wave states: the monoid rule, through LDS
   const float l_tot = halves_sum(l_run);
   __syncthreads();  // every wave is done with its tile buffers
-  float* f_acc = (float*)smem;                        // [kWaves][g][D]
-  float* f_m = f_acc + kWaves * 32 * D;               // [kWaves][32]
-  float* f_l = f_m + kWaves * 32;                     // [kWaves][32]
+  float* f_acc = (float*)smem;                        // [NWV][g][D]
+  float* f_m = f_acc + NWV * 32 * D;               // [NWV][32]
+  float* f_l = f_m + NWV * 32;                     // [NWV][32]
   if (l32 < a.g) {
 #pragma unroll
     for (int cb = 0; cb < D / 32; cb++)
@@ -315,14 +317,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_kernel(DecArgs 
   }
   __syncthreads();
   const int total = a.g * D;
-  for (int e = threadIdx.x; e < total; e += kWaves * 64) {
+  for (int e = threadIdx.x; e < total; e += NWV * 64) {
     const int qh = e / D, col = e % D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, f_m[w * 32 + qh]);
+    for (int w = 0; w < NWV; w++) M = fmaxf(M, f_m[w * 32 + qh]);
     float L = 0.0f, A = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) {
+    for (int w = 0; w < NWV; w++) {
       const float mw = f_m[w * 32 + qh];
       const float f = (mw == kNegInf) ? 0.0f : fast_exp2(mw - M);
       L += f * f_l[w * 32 + qh];
@@ -591,12 +593,24 @@ hipError_t launch(const DecodeProblem& p, hipStream_t s) {
   a.page = (int)p.page;
   a.max_pages = (int)p.max_pages;
   a.num_pages = (int)p.num_pages;
-  if (p.block_table != nullptr)
-    hipLaunchKernelGGL((decode_partial_kernel<D, true>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
-  else if (p.k8 != nullptr)
+  // Dense bf16 caches: 4-wave workgroups (one per CU) while the grid fits the
+  // 256 CUs; beyond that 2-wave workgroups, two per CU, so that the whole
+  // grid starts at once instead of in one and a half rounds (48 streams x 8
+  // kv heads: 2-10 % faster at 512..4096 keys; 2-wave workgroups on a grid of
+  // at most 256 leave half the CU slots empty and measured 2-16 % slower).
+  // Paged caches keep 4 waves: their streams differ in length, the longest
+  // stream's chunks decide the end, and a 2-wave workgroup streams a chunk at
+  // half the rate (14 % slower at 48 streams of 512..4096 keys).
+  const bool two = a.n_wgs > 256;
+  if (p.block_table != nullptr) {
+    hipLaunchKernelGGL((decode_partial_kernel<D, true, 4>), dim3(a.n_wgs), dim3(256), 0, s, a);
+  } else if (p.k8 != nullptr) {
     hipLaunchKernelGGL((decode_partial_fp8_kernel<D>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_partial_kernel<D, false>), dim3(a.n_wgs), dim3(kWaves * 64), 0, s, a);
+  } else if (two) {
+    hipLaunchKernelGGL((decode_partial_kernel<D, false, 2>), dim3(a.n_wgs), dim3(128), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_partial_kernel<D, false, 4>), dim3(a.n_wgs), dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.S == 1 || a.counters != nullptr) return e;
   const int rows = a.B * a.Hq;
