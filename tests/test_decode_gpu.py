@@ -67,6 +67,26 @@ def test_ragged_shapes(oracle_mod, shape):
     check(oracle_mod, q, k, v, num_splits=3)
 
 
+# grids of more than 256 workgroups run the two-wave kernel (two workgroups per
+# CU); ragged key counts and chunk ends, d = 64 and 128, g = 4 and 8
+TWO_WAVE = [
+    # B, Hq, Hkv, L, d, num_splits
+    (40, 32, 8, 1000, 128, 0),     # 320 workgroups, one chunk each
+    (48, 32, 8, 999, 64, 0),
+    (12, 64, 8, 1500, 128, 3),     # 288 workgroups of three chunks per stream
+]
+
+
+@pytest.mark.parametrize("shape", TWO_WAVE)
+def test_two_wave_grids(oracle_mod, shape):
+    B, Hq, Hkv, L, d, S = shape
+    plan = am.decode_num_splits(B, Hq, Hkv, L, d) if S == 0 else S
+    assert B * Hkv * plan > 256
+    print(f"two-wave decode B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} splits={plan}", flush=True)
+    q, k, v = inputs(3700 + L + d, B, Hq, Hkv, L, d)
+    check(oracle_mod, q, k, v, num_splits=S)
+
+
 def test_peaked(oracle_mod):
     q, k, v = inputs(3700, 4, 32, 8, 2048, 128, peak=6.0)
     check(oracle_mod, q, k, v)
