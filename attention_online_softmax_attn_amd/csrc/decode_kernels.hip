@@ -298,12 +298,12 @@ __global__ __launch_bounds__(NWV * 64, 1) void decode_partial_kernel(DecArgs a) 
     step(i + 1, w1, w1 + TILE_BYTES, w0, w0 + TILE_BYTES);
   }
 
-  // ---- fold the four wave states: the monoid rule, through LDS
+  // ---- fold the wave states: the monoid rule, through LDS
   const float l_tot = halves_sum(l_run);
   __syncthreads();  // every wave is done with its tile buffers
-  float* f_acc = (float*)smem;                        // [NWV][g][D]
-  float* f_m = f_acc + NWV * 32 * D;               // [NWV][32]
-  float* f_l = f_m + NWV * 32;                     // [NWV][32]
+  float* f_acc = (float*)smem;  // [NWV][g][D]
+  float* f_m = f_acc + NWV * 32 * D;  // [NWV][32]
+  float* f_l = f_m + NWV * 32;  // [NWV][32]
   if (l32 < a.g) {
 #pragma unroll
     for (int cb = 0; cb < D / 32; cb++)
