@@ -155,3 +155,28 @@ def test_bf16_grads_c5_tolerance_study(oracle_mod):
         # the rounding adds no more than half an ulp at the largest magnitude
         assert e16 <= e32 + 2.0 ** -9 * gmax * 1.0001
         print(f"  {name}: max|g| {gmax:.3f}  err fp32 {e32:.3e}  err bf16 {e16:.3e}", flush=True)
+
+
+def test_eight_wave_dq_ragged_gqa(oracle_mod):
+    # 2 x 32 query heads over 8 kv heads at 2100 rows: 576 query tiles of 256
+    # rows, so dQ runs as eight-wave workgroups, with a ragged last tile and
+    # four query heads accumulated into each kv head's dK and dV
+    B, Hq, Hkv, N, d = 2, 32, 8, 2100, 128
+    assert B * Hq * ((N + 255) // 256) >= 512
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = synth.attn_inputs(5700, B, Hq, Hkv, N, N, d, bf16=True, with_dout=True)
+    print("eight-wave dQ, ragged GQA: launching", flush=True)
+    gq, gk, gv = gpu_grads(q, k, v, do, True, scale)
+    # one kv head in full (its four query heads) in each batch entry
+    for b, kvh in ((0, 0), (1, Hkv - 1)):
+        hs = list(range(kvh * 4, kvh * 4 + 4))
+        eq, ek, ev = oracle_mod.bwd(np.ascontiguousarray(q[b:b + 1, hs]), np.ascontiguousarray(k[b:b + 1, kvh:kvh + 1]),
+                                    np.ascontiguousarray(v[b:b + 1, kvh:kvh + 1]), np.ascontiguousarray(do[b:b + 1, hs]),
+                                    scale, True)
+        assert_close("dQ", gq[b:b + 1, hs], eq, TOL_GRAD)
+        assert_close("dK", gk[b:b + 1, kvh:kvh + 1], ek, TOL_GRAD)
+        assert_close("dV", gv[b:b + 1, kvh:kvh + 1], ev, TOL_GRAD)
+    # over every kv head: sum_j dK_j = 0 and sum_j dV_j = sum over its query heads and rows of dO
+    assert np.max(np.abs(gk.sum(axis=2))) <= 0.5
+    sdo = do.astype(np.float64).reshape(B, Hkv, 4, N, d).sum(axis=(2, 3))
+    assert np.max(np.abs(gv.sum(axis=2) - sdo)) <= 0.5
