@@ -570,13 +570,17 @@ hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
   }
   if (p.bf16) {
     // 8 waves (256 query rows) per workgroup, which share each K/V tile (half
-    // the tile loads and barriers per query row of the 4-wave configuration),
-    // once there are at least two such workgroups per CU over the launch:
-    // measured 3-8 % faster at N = 4096 and 8192 (32 heads) and 2.6 % at
-    // 4 x 16 heads x 2048, 14 % slower with one per CU (N = 2048, 32 heads),
-    // where 4-wave workgroups, two per CU, fill the machine instead.
+    // the tile loads and barriers per query row of the 4-wave configuration).
+    // Dense problems take them once there are at least two such workgroups
+    // per CU over the launch: measured 3-8 % faster at N = 4096 and 8192 (32
+    // heads) and 2.6 % at 4 x 16 heads x 2048, 14 % slower with one per CU
+    // (N = 2048, 32 heads), where 4-wave workgroups, two per CU, fill the
+    // machine instead.  Packed batches, whose grid counts every sequence at
+    // the longest one's length, keep 4 waves up to 8 per CU (8 waves measured
+    // 9 % slower on 4 sequences of 600..2048 tokens, equal on 8).
     constexpr int NWB = ATTN_FWD_BIG_NW, BNB = ATTN_FWD_BIG_BN;
-    const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= 2 * 256;
+    const int64_t min_big = p.cu_q != nullptr ? 8 * 256 : 2 * 256;
+    const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= min_big;
     if (p.d == 128) {
       if (big) return causal ? launch_bf16<128, NWB, BNB, true>(p, s) : launch_bf16<128, NWB, BNB, false>(p, s);
       return causal ? launch_bf16<128, 4, 64, true>(p, s) : launch_bf16<128, 4, 64, false>(p, s);
