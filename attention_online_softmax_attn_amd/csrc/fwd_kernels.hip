@@ -254,15 +254,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       }
     }
     if (need_mask) {
+      // key j = j0 + 4h + c (c = kb*32 + 8(r/4) + r%4, a constant per
+      // element) is visible iff j < Nk and, causal, j <= qi + off: one lane
+      // bound lim on c, so each element costs one compare with a constant
+      const int lim = (CAUSAL ? min(Nk, qi + off + 1) : Nk) - j0 - 4 * h32;
 #pragma unroll
       for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          bool ok = j < Nk;
-          if (CAUSAL) ok = ok && (j <= qi + off);
-          if (!ok) st[kb][r] = kNegInf;
-        }
+        for (int r = 0; r < 16; r++)
+          if (!(kb * 32 + 8 * (r >> 2) + (r & 3) < lim)) st[kb][r] = kNegInf;
     }
     // online softmax.  P goes to bf16 (the MFMA operand); the row sum adds the
     // fp32 values (a sum of the bf16 values would move LSE by up to 2^-9 on
