@@ -138,17 +138,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
       st = mfma32(*(const bf16x8*)(kt + aoff[s]), qf[s], st);
       dpt = mfma32(*(const bf16x8*)(vt + aoff[s]), df[s], dpt);
     }
-    // dS^T = P^T o (dP^T - D); keys j0 + 8(r/4) + 4h + r%4
+    // dS^T = P^T o (dP^T - D); keys j0 + 4h + c, c = 8(r/4) + r%4.  Key j is
+    // visible iff the row exists, j < Nk and, causal, j <= qi + off: one lane
+    // bound lim on c, so a masked element costs one compare with a constant
+    const int lim = q_in ? (CAUSAL ? min(a.Nk, qi + off + 1) : a.Nk) - j0 - 4 * h32 : 0;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const float p = fast_exp2(__builtin_fmaf(st[r], a.c, -l2q));
       float ds = p * (dpt[r] - ddq);
-      if (need_mask) {
-        const int j = j0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-        bool ok = q_in && (j < a.Nk);
-        if (CAUSAL) ok = ok && (j <= qi + off);
-        ds = ok ? ds : 0.0f;
-      }
+      if (need_mask) ds = (8 * (r >> 2) + (r & 3) < lim) ? ds : 0.0f;
       dpt[r] = ds;
     }
     // dQ^T += K^T dS^T, 16 keys per MFMA (K read transposed)
