@@ -128,6 +128,17 @@ def _dims(q, k, v):
     return B, Hq, k.shape[1], Nq, k.shape[2], d
 
 
+def _want(t, shape, dtype, name: str):
+    """A caller-supplied buffer must have exactly the shape and dtype the call
+    writes or reads: the kernels take its address and trust the sizes."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
@@ -136,6 +147,8 @@ def attn_fwd(q, k, v, causal: bool = False, scale=None, out=None, lse=None, want
     """Fused forward.  Returns (o, lse); lse is None when want_lse is False."""
     _check_dev(q, k, v, out, lse)
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Nq), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
@@ -167,6 +180,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, caus
     if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of the same length n_seqs + 1")
     n_seqs = cu_seqlens_q.shape[0] - 1
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (Hq, total_q), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
@@ -191,6 +206,8 @@ def attn_decode_splitkv(q, k, v, scale=None, num_splits: int = 0, workspace=None
     """Split-KV decode (q has Nq = 1).  Returns (o, lse)."""
     _check_dev(q, k, v, out, lse, workspace)
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Nq), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
@@ -222,6 +239,8 @@ def attn_decode_splitkv_fused(q, k, v, scale=None, num_splits: int = 0, workspac
     allocated.  Returns (o, lse)."""
     _check_dev(q, k, v, out, lse, workspace)
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Nq), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
@@ -255,6 +274,8 @@ def attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, scale=None, num_splits:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k8 {tuple(k8.shape)}")
     if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32 or k_scale.numel() != Hkv or v_scale.numel() != Hkv:
         raise ValueError("k_scale and v_scale must be fp32 with one value per kv head")
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Nq), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
@@ -294,6 +315,8 @@ def attn_fwd_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_le
     for t in (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k):
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (Hq, total_q), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
@@ -326,6 +349,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: i
     for t in (q, k_cache, v_cache, block_table, seq_lens):
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Nq), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
@@ -356,9 +381,12 @@ def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale=None, workspace=
         raise ValueError(f"attn_bwd: grad_dtype must be float32 or bfloat16, not {gdt}")
     _check_dev(q, k, v, o, dout, lse, workspace, dq, dk, dv)
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
-    for g in (dq, dk, dv):
-        if g is not None and g.dtype != gdt:
-            raise ValueError(f"attn_bwd: gradient buffers must be {gdt}")
+    _want(o, q.shape, q.dtype, "o")
+    _want(dout, q.shape, q.dtype, "dout")
+    _want(lse, (B, Hq, Nq), torch.float32, "lse")
+    _want(dq, q.shape, gdt, "dq")
+    _want(dk, k.shape, gdt, "dk")
+    _want(dv, v.shape, gdt, "dv")
     gd = dict(dtype=gdt, device=q.device)
     dq = torch.empty(q.shape, **gd) if dq is None else dq
     dk = torch.empty(k.shape, **gd) if dk is None else dk

@@ -85,6 +85,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int KB = KS / 32;                  // 32-key blocks per sub-tile
   static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly over the workgroup");
   static_assert(BN % KS == 0, "BN must be a multiple of 64");
+  // the paged cache's pages are whole multiples of 64 keys (checked by the C
+  // ABI), so a 64-key tile never straddles two pages; a larger tile could
+  static_assert(!PAGED || BN == 64, "paged key tiles must be 64 keys");
   static_assert(TILE_BYTES <= 65536, "LDS offsets must fit the 16-bit immediate");
 
   // Two stages of one K and one V tile each; tile t uses stage t % 2.  Every

@@ -193,6 +193,81 @@ def setup(paths):
     return st
 
 
+def _sysfs_card():
+    """sysfs directory of the GPU torch uses (matched by PCI bus id), or None."""
+    import glob
+
+    import torch
+
+    try:
+        props = torch.cuda.get_device_properties(0)
+        bus = getattr(props, "pci_bus_id", None)
+    except Exception:
+        bus = None
+    cards = []
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        if not os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+            continue
+        try:
+            addr = os.path.basename(os.path.realpath(dev))  # e.g. 0000:05:00.0
+            cards.append((int(addr.split(":")[1], 16), dev))
+        except (ValueError, IndexError):
+            cards.append((None, dev))
+    if bus is not None:
+        for b, dev in cards:
+            if b == bus:
+                return dev
+    return cards[0][1] if len(cards) == 1 else None
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (sysfs pp_dpm_sclk, the level
+    marked '*') every few milliseconds while the timed steps run, so that the
+    line can state the clock the kernels actually ran at."""
+
+    def __init__(self, period_s=0.005):
+        import threading
+
+        self.dev = _sysfs_card()
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            for line in open(os.path.join(self.dev, "pp_dpm_sclk")):
+                if "*" in line:
+                    return float(line.split(":")[1].strip().lower().replace("*", "").replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def __enter__(self):
+        if self.dev is not None:
+            self._t.start()
+        return self
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.dev is not None:
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"source": "sysfs pp_dpm_sclk, sampled every 5 ms over the timed steps", "samples": len(xs),
+                "mhz_median": xs[len(xs) // 2], "mhz_min": xs[0], "mhz_max": xs[-1]}
+
+
 def run_gpu(paths, steps, warmup):
     import torch
 
@@ -288,14 +363,16 @@ def run_gpu(paths, steps, warmup):
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        ev[s][0].record()
-        for i, p in enumerate(order):
-            run_path(p)
-            ev[s][i + 1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for s in range(steps):
+            ev[s][0].record()
+            for i, p in enumerate(order):
+                run_path(p)
+                ev[s][i + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    st["sclk"] = clk.summary()
     per = {p: [] for p in order}
     for s in range(steps):
         for i, p in enumerate(order):
@@ -314,6 +391,7 @@ def cpu_baseline(st, paths, budget_s):
     flops = 0.0
     secs = 0.0
     parts = []
+    fwd_rate = None
     # the oracle leg covers the default step's paths (not the opt-in varlen one)
     share = budget_s / max(1, len([p for p in paths if p in ("fwd", "decode", "bwd")]))
     if "fwd" in paths:
@@ -322,16 +400,20 @@ def cpu_baseline(st, paths, budget_s):
         rng_seed = 40004
         n, done_rows = 64, 0
         t_fwd = 0.0
+        fwd_flops_done = 0.0
         while t_fwd < share:
             rows = synth.sample_rows(rng_seed + done_rows, n, c["B"], c["Hq"], c["N"])
             t = time.perf_counter()
             oracle.fwd_rows(q, k, v, rows, 1.0 / math.sqrt(c["d"]), True)
             t_fwd += time.perf_counter() - t
-            flops += float(np.sum(4.0 * c["d"] * (rows[:, 2] + 1)))
+            f_rows = float(np.sum(4.0 * c["d"] * (rows[:, 2] + 1)))
+            flops += f_rows
+            fwd_flops_done += f_rows
             done_rows += n
             n *= 2
         secs += t_fwd
         parts.append(f"{done_rows} random query rows of the N=44032 causal prefill")
+        fwd_rate = fwd_flops_done / t_fwd
     if "decode" in paths:
         c = DECODE
         q, k, v = st["decode_host"]
@@ -358,13 +440,61 @@ def cpu_baseline(st, paths, budget_s):
             heads += n
         secs += t_bwd
         parts.append(f"the backward of {heads} of the 64 (batch, head) problems at N=2048")
-    return {
+    out = {
         "value": round(flops / secs / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": "; ".join(parts) + f" ({secs:.1f} s of fp64 CPU work)",
+        "cpu_model": cpu_model(),
     }
+    if fwd_rate:
+        c = PREFILL
+        full = fwd_flops(c["B"], c["Hq"], c["N"], c["N"], c["d"], True)
+        out["prefill_full_size_s_extrapolated"] = round(full / fwd_rate, 1)
+    one = single_thread_run(st, paths)
+    if one is not None:
+        out["single_thread"] = one
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def single_thread_run(st, paths):
+    """The oracle at one OpenMP thread on the whole decode of the step (48
+    streams x 4096 keys), for reference beside the all-cores figure."""
+    import ctypes
+
+    import oracle
+
+    if "decode" not in paths:
+        return None
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    c = DECODE
+    q, k, v = st["decode_host"]
+    nb = c["B"]
+    n_all = oracle.num_threads()
+    gomp.omp_set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        oracle.fwd(q[:nb], k[:nb], v[:nb], 1.0 / math.sqrt(c["d"]), False)
+        secs = time.perf_counter() - t
+    finally:
+        gomp.omp_set_num_threads(n_all)
+    f = decode_flops(nb, c["Hq"], c["L"], c["d"])
+    return {"value": round(f / secs / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "sample": f"the full {nb}x{c['L']} decode at one thread ({secs:.1f} s)"}
 
 
 def copy_probe(mib):
@@ -386,6 +516,8 @@ def copy_probe(mib):
 # its own with percentiles (fwd and bwd >= 50 % of bf16 MFMA at N >= 2048,
 # decode >= 70 % of HBM where its KV cache is >= 256 MiB)
 SWEEP_FWD = [(1, 32, 8, n) for n in (2048, 4096, 8192, 16384, 44032)] + [(4, 16, 16, 2048)]
+# the transformer-block forward (B=4, H=8, N=512, d=64), causal and not: reported, no target
+SWEEP_SMALL = [(4, 8, 8, 512, 64, True), (4, 8, 8, 512, 64, False)]
 SWEEP_DECODE = [(b, n) for b in (1, 16, 48) for n in (512, 1024, 2048, 4096)]
 POOL_BYTES = 512 << 20  # inputs rotate over copies of at least this size (twice the 256 MB MALL)
 
@@ -448,6 +580,19 @@ def sweep():
         emit({"path": "fwd", "shape": f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal", "copies": n, **t,
               "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "target": 0.5,
               "meets": tf / PEAK_BF16_TFLOPS >= 0.5})
+        del qs, o, lse
+    for B, Hq, Hkv, N, d, causal in SWEEP_SMALL:
+        per_copy = 2 * B * (Hq + 2 * Hkv) * N * d
+        n = max(1, -(-POOL_BYTES // per_copy))
+        qs = [(rnd(B, Hq, N, d), rnd(B, Hkv, N, d), rnd(B, Hkv, N, d)) for _ in range(n)]
+        o = torch.empty_like(qs[0][0])
+        lse = torch.empty(B, Hq, N, dtype=torch.float32, device="cuda")
+        t = time_calls(lambda i: am.attn_fwd(*qs[i], causal=causal, out=o, lse=lse), n)
+        f = fwd_flops(B, Hq, N, N, d, causal)
+        tf = f / t["ms_median"] / 1e9
+        emit({"path": "fwd", "shape": f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} " + ("causal" if causal else "non-causal"),
+              "copies": n, **t, "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4),
+              "target": None, "meets": None})
         del qs, o, lse
     # backward at B=4 H=16 N=2048 (O and LSE from the forward, outside the timing)
     c = BACKWARD
@@ -647,6 +792,7 @@ def main():
         "timer_check": {"event_ms_per_step": round(ms_step, 4), "wall_ms_per_step": round(wall_ms, 4),
                         "agree": abs(wall_ms - ms_step) <= 0.1 * ms_step + 0.05},
         "sane": sane,
+        "sclk": st.get("sclk"),
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(st, paths, args.cpu_seconds)

@@ -69,6 +69,16 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * lse [B,Hq,Nq] fp32 (may be NULL when not needed).  dtype ATTN_BF16 runs the
  * contractions on bf16 MFMA; ATTN_F32 on fp32 MFMA.  Causal key blocks that
  * no query of a tile can see are neither loaded nor computed.
+ *   Source   "Não escreva kernels, derive-os", section "Aprofundamento",
+ *            first paragraph: flash attention as a fusion obtained once the
+ *            streaming softmax is seen as a reduction under a monoid; the
+ *            key tiles of a query tile are folded left to right in that
+ *            monoid, in one pass.  "Tang Project Derives GPU Kernels via IR
+ *            ...", section "Details": causal forward passes and the 44k-token
+ *            prefill.
+ *   Sizes    ATTN_F32 is a correctness path (one wave per workgroup, no
+ *            pipelining): use it for small problems; ATTN_BF16 is the
+ *            throughput path.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
                      int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, attn_dtype dtype,
@@ -145,6 +155,16 @@ attn_status attn_fwd_varlen_paged(const void* q, const void* k_cache, const void
  * attn_decode_workspace_bytes(..., num_splits) is enough for this entry point,
  * for attn_decode_splitkv_fp8 (whose plan models the FP8 kernel) and for
  * attn_decode_paged (Nk = its max_seq_len) at the same num_splits.
+ *   Source   the merge is the online-softmax monoid of "Não escreva kernels,
+ *            derive-os" (section "Aprofundamento", first paragraph): any
+ *            grouping of the chunks gives the same state up to rounding.
+ *            "Tang Project Derives GPU Kernels via IR ..." (section
+ *            "Details") measures decode at 16-48 concurrent streams and ties
+ *            an accuracy miss to the split granularity.
+ *   Workspace [B, Hq, S, d] fp32 accumulators then [B, Hq, S, 2] fp32
+ *            (m in log2 units, l), each 256-byte aligned; owned by the
+ *            caller, not read across calls; NULL is accepted when the plan
+ *            has one chunk (attn_decode_workspace_bytes returns 0).
  */
 int attn_decode_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d);
 size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits);
@@ -244,6 +264,16 @@ attn_status attn_decode_splitkv_fp8(const void* q, const void* k, const void* v,
  * dv sum over the query heads that share a kv head).  The workspace holds one
  * 8-byte record per query row, (LSE * log2 e, D_i = dO_i . O_i), with the rows
  * of each head padded to a multiple of 128.  Only ATTN_BF16 is built.
+ *   Source   "Não escreva kernels, derive-os", FAQ entry "O que o Tang propõe
+ *            de diferente?": the backward is obtained by rewriting the same
+ *            fused expression; section "Aprofundamento", third paragraph: a
+ *            fused bf16 backward missed an fp32 tolerance, so the gradients
+ *            are accumulated and written in fp32 here.  The pages print no
+ *            formula: with P = exp(scale Q K^T - LSE) (masked),
+ *            dV = P^T dO, dS = P o (dO V^T - rowsum(dO o O)), dQ = scale dS K,
+ *            dK = scale dS^T Q, the textbook gradient of softmax attention.
+ *   Result   deterministic: every gradient element has one writer, so
+ *            repeated calls give the same bits.
  */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d);
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

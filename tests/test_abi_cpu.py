@@ -367,3 +367,16 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         am.attn_fwd(q, q, q)
+
+
+def test_binding_rejects_mis_sized_caller_buffers():
+    # caller-supplied outputs and inputs must match the shape and dtype the
+    # call uses: a wrong one is refused before any address reaches the library
+    import torch
+
+    am._want(None, (2, 3), torch.float32, "x")
+    am._want(torch.empty(2, 3), (2, 3), torch.float32, "x")
+    with pytest.raises(ValueError):
+        am._want(torch.empty(2, 4), (2, 3), torch.float32, "x")
+    with pytest.raises(TypeError):
+        am._want(torch.empty(2, 3, dtype=torch.bfloat16), (2, 3), torch.float32, "x")
