@@ -30,7 +30,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
 
-ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP, ATTN_ERR_SCRATCH = range(6)
+DECODE_SCRATCH_BYTES = 8 << 20  # ATTN_DECODE_SCRATCH_BYTES
 ATTN_F32, ATTN_BF16 = 0, 1
 
 _lib = None
@@ -69,6 +70,10 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_fused_workspace_bytes.restype = sz
     L.attn_decode_splitkv_fused.argtypes = L.attn_decode_splitkv.argtypes
     L.attn_decode_splitkv_fused.restype = ci
+    L.attn_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci, ci, vp]
+    L.attn_decode_splitkv_noalloc.restype = ci
+    L.attn_decode_noalloc_scratch_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
+    L.attn_decode_noalloc_scratch_bytes.restype = sz
     L.attn_fwd_varlen_paged.argtypes = [vp] * 8 + [i64] * 10 + [f32, ci, vp]
     L.attn_fwd_varlen_paged.restype = ci
     L.attn_decode_paged.argtypes = [vp] * 7 + [i64] * 8 + [f32, ci, vp, sz, vp]
@@ -221,6 +226,28 @@ def attn_decode_splitkv(q, k, v, scale=None, num_splits: int = 0, workspace=None
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_splitkv")
     return o, (lse if want_lse else None)
+
+
+def decode_noalloc_scratch_bytes(B: int, Hq: int, Hkv: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    return int(lib().attn_decode_noalloc_scratch_bytes(B, Hq, Hkv, Nk, d, num_splits))
+
+
+def attn_decode_splitkv_noalloc(q, k, v, out, lse=None, scale=None, num_splits: int = 0):
+    """attn_decode_splitkv with the partial states in the library's fixed
+    device scratch: no workspace, and the C call allocates nothing.  The
+    caller passes the outputs (out like q; lse fp32 [B, Hq, 1] or None).
+    Calls that overlap on one GPU race on the scratch."""
+    _check_dev(q, k, v, out, lse)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    if out is None:
+        raise ValueError("attn_decode_splitkv_noalloc: the caller passes out")
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Nq), torch.float32, "lse")
+    st = lib().attn_decode_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                           _scale(scale, d), 0, int(num_splits), _dtype_code(q), _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_splitkv_noalloc")
+    return out, lse
 
 
 def decode_fused_num_splits(B: int, Hq: int, Hkv: int, Nk: int, d: int) -> int:

@@ -116,6 +116,8 @@ const char* attn_strerror(attn_status status) {
       return "workspace missing or too small";
     case ATTN_ERR_HIP:
       return "HIP launch failed";
+    case ATTN_ERR_SCRATCH:
+      return "the split plan needs more than the fixed scratch of the allocation-free entry point";
   }
   return "unknown status";
 }
@@ -210,6 +212,7 @@ extern "C" {
 size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
   if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128) || num_splits < 0) return 0;
   // enough for the bf16, FP8 and paged entry points' plans
+  static_assert(attn::kDecodeScratchBytes == ATTN_DECODE_SCRATCH_BYTES, "one scratch size");
   return std::max({partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, false)),
                    partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, true)),
                    partial_bytes(B, Hq, Hkv, d, paged_plan(B, Hkv, Nk, d, num_splits))});
@@ -229,7 +232,7 @@ namespace {
 attn_status decode_common(const void* q, const void* k, const void* v, const float* k_scale, const float* v_scale,
                           bool fp8, bool fused, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                           int64_t d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
-                          attn_dtype dtype, void* stream) {
+                          attn_dtype dtype, void* stream, bool use_scratch = false) {
   attn_status st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (num_splits < 0) return ATTN_ERR_INVALID;
@@ -256,6 +259,12 @@ attn_status decode_common(const void* q, const void* k, const void* v, const flo
   p.chunk = sp.chunk;
   if (sp.splits > 1) {
     const size_t need = (fused ? kDecodeCountBytes : 0) + partial_bytes(B, Hq, Hkv, d, sp);
+    if (use_scratch) {
+      // the library's fixed device scratch instead of a caller workspace
+      if (need > ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+      if (attn::decode_scratch(&workspace) != hipSuccess) return ATTN_ERR_HIP;
+      workspace_bytes = ATTN_DECODE_SCRATCH_BYTES;
+    }
     if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     // the arrival counts take device atomics: 4-byte alignment
     if (fused && ((uintptr_t)workspace & 3) != 0) return ATTN_ERR_INVALID;
@@ -289,6 +298,19 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
   (void)causal;  // one bottom-right-aligned query sees every key
   return decode_common(q, k, v, nullptr, nullptr, false, false, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits, workspace,
                        workspace_bytes, dtype, stream);
+}
+
+attn_status attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                        int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                        int causal, int num_splits, attn_dtype dtype, void* stream) {
+  (void)causal;
+  return decode_common(q, k, v, nullptr, nullptr, false, false, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, num_splits,
+                       nullptr, 0, dtype, stream, true);
+}
+
+size_t attn_decode_noalloc_scratch_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits) {
+  if (!dims_ok(B, Hq, Hkv, 1, Nk) || (d != 64 && d != 128) || num_splits < 0) return 0;
+  return partial_bytes(B, Hq, Hkv, d, plan_splits(B, Hkv, Nk, d, num_splits, false, false));
 }
 
 attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,

@@ -20,6 +20,8 @@
 // concurrent streams is the one "Tang Project Derives GPU Kernels via IR ..."
 // reports in its "Details" section.  Regrouping a monoid fold does not change
 // its value, so any split count gives the same result up to rounding.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -620,8 +622,37 @@ hipError_t launch(const DecodeProblem& p, hipStream_t s) {
 
 }  // namespace
 
+// Fixed scratch for the decode entry point that allocates nothing: the
+// partial states of its split plan live here instead of in a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends, and every call on that GPU shares it, so calls that overlap
+// on one GPU race (stream order keeps them apart).  Host code never uses the
+// array's name as an address: decode_scratch() looks the device address up.
+static __device__ __attribute__((aligned(256))) char scratch[kDecodeScratchBytes];
+
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t s) {
   return p.d == 128 ? launch<128>(p, s) : launch<64>(p, s);
+}
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // once per device, with that device current: each device's copy of the
+    // array sits at its own address
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attn

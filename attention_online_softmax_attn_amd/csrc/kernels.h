@@ -70,6 +70,12 @@ struct DecodeProblem {
 // Keys per decode tile; split chunks are whole multiples of it.
 constexpr int kDecodeTile = 32;
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t s);
+// Bytes of the decode's fixed device scratch (the allocation-free entry
+// point's partial states); ATTN_DECODE_SCRATCH_BYTES in attn.h.
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+// Device address of the current device's copy of that scratch (looked up
+// once per device).
+hipError_t decode_scratch(void** ptr);
 
 struct BwdProblem {
   const void* q;

@@ -59,7 +59,8 @@ typedef enum {
   ATTN_ERR_INVALID = 1,     /* null pointer, negative size, Hq % Hkv != 0, bad scale or dtype */
   ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64,128}, size above ATTN_MAX_SEQ, dtype */
   ATTN_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than required */
-  ATTN_ERR_HIP = 4          /* a kernel launch failed */
+  ATTN_ERR_HIP = 4,         /* a kernel launch failed */
+  ATTN_ERR_SCRATCH = 5      /* the allocation-free decode needs more than ATTN_DECODE_SCRATCH_BYTES */
 } attn_status;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -172,6 +173,25 @@ attn_status attn_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
                                 int num_splits, void* workspace, size_t workspace_bytes, attn_dtype dtype,
                                 void* stream);
+
+/*
+ * attn_decode_splitkv for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels,
+ * split plan and bits.  The partial states live in a fixed device array of
+ * ATTN_DECODE_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; the call allocates and frees nothing.  A plan
+ * whose partial states exceed it (attn_decode_noalloc_scratch_bytes, the same
+ * as attn_decode_workspace_bytes of the bf16 plan) returns ATTN_ERR_SCRATCH
+ * before any HIP call.  Every call on one GPU shares its array, so calls
+ * that overlap on one GPU race: order them on one stream (or wait between
+ * streams).  Nothing in the array needs to start at zero.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+size_t attn_decode_noalloc_scratch_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, int num_splits);
+attn_status attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                        int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                        int causal, int num_splits, attn_dtype dtype, void* stream);
 
 /*
  * Split-KV decode in one launch.  Same arguments, rules and result as

@@ -380,3 +380,35 @@ def test_binding_rejects_mis_sized_caller_buffers():
         am._want(torch.empty(2, 4), (2, 3), torch.float32, "x")
     with pytest.raises(TypeError):
         am._want(torch.empty(2, 3, dtype=torch.bfloat16), (2, 3), torch.float32, "x")
+
+
+def decn(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=32, Hkv=8, Nq=1, Nk=4096, d=128, scale=0.088, splits=0,
+         dt=am.ATTN_BF16):
+    return am.lib().attn_decode_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, 0, splits, dt, None)
+
+
+@no_gpu
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(Nq=2), am.ATTN_ERR_INVALID),
+        (dict(splits=-1), am.ATTN_ERR_INVALID),
+        (dict(q=NUL), am.ATTN_ERR_INVALID),
+        (dict(dt=am.ATTN_F32), am.ATTN_ERR_UNSUPPORTED),
+        (dict(d=80), am.ATTN_ERR_UNSUPPORTED),
+        # 16 x 32 rows x 64 chunks of partial states (~17 MB) exceed the fixed scratch
+        (dict(B=16, splits=64), am.ATTN_ERR_SCRATCH),
+    ],
+)
+def test_decode_noalloc_rejects(kw, code):
+    assert decn(**kw) == code
+
+
+def test_decode_noalloc_scratch_sizes():
+    # the scratch holds what the two-launch decode's workspace would, and the
+    # size check matches the header's bound
+    for args in ((1, 32, 8, 4096, 128, 0), (3, 32, 8, 3000, 128, 5), (16, 32, 8, 4096, 128, 64)):
+        assert am.decode_noalloc_scratch_bytes(*args) <= am.decode_workspace_bytes(*args)
+    assert am.decode_noalloc_scratch_bytes(16, 32, 8, 4096, 128, 64) > am.DECODE_SCRATCH_BYTES
+    assert am.decode_noalloc_scratch_bytes(48, 32, 8, 4096, 128, 0) == 0  # one chunk: no scratch read
+    assert "scratch" in am.strerror(am.ATTN_ERR_SCRATCH)
