@@ -75,6 +75,126 @@ __device__ __forceinline__ int snake_pid(int pid, int n, int on) {
   return x + 8 * (t < half ? t : T - 1 - (t - half));
 }
 
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Packed variable-length batch: the work item (sequence, query tile, query
+// head) of launch index `rank` in a longest-first order, computed by every
+// wave from the sequence offsets alone (no workspace, no host round trip).
+// An item's weight is the number of BN-key tiles its workgroup streams, the
+// kernel's own count: W(s, t) = ceil(min(Lk, min((t+1) BM, Lq) + Lk - Lq) / BN)
+// when causal (at least 0), ceil(Lk / BN) otherwise; it does not decrease with
+// t.  For a threshold w the items of sequence s with W >= w are its last
+// c_s(w) tiles, c_s(w) in closed form, so the weight of rank r is found by a
+// binary search on w over sum_s c_s(w), and ties go in (sequence, tile) order.
+// Within an item the Hq heads take consecutive ranks, kv head first
+// (j -> kv head j % Hkv), so that the dispatcher, which sends launch index i
+// to XCD i % 8, keeps the query heads of one kv head together when Hkv is 8.
+// Returns false for a rank past the last item.
+template <int BM, int BN, bool CAUSAL, bool PAGED>
+__device__ bool varlen_item(const FwdArgs& a, int rank, int& s_out, int& qt_out, int& h_out) {
+  const int lane = threadIdx.x & 63;
+  const int n_seqs = a.B;
+  constexpr int kCached = 4;  // sequences 0 .. 255 stay in registers
+  // the kernel's own clamped per-sequence sizes
+  auto sizes = [&](int s, int& lq, int& lk) {
+    const int q1 = min(a.cu_q[s + 1], a.tot_q), q0 = max(0, min(a.cu_q[s], q1));
+    lq = q1 - q0;
+    if constexpr (PAGED) {
+      lk = min(max(a.seq_lens_k[s], 0), min(a.Nk, a.max_pages * a.page));
+    } else {
+      const int k1 = min(a.cu_k[s + 1], a.tot_k), k0 = max(0, min(a.cu_k[s], k1));
+      lk = k1 - k0;
+    }
+  };
+  int lq_c[kCached], lk_c[kCached];
+#pragma unroll
+  for (int c = 0; c < kCached; c++) {
+    lq_c[c] = 0;
+    lk_c[c] = 0;
+    const int s = c * 64 + lane;
+    if (s < n_seqs) sizes(s, lq_c[c], lk_c[c]);
+  }
+  auto get = [&](int c, int& lq, int& lk) {
+    if (c < kCached) {
+      // constant-indexed copies, so that the arrays stay in registers
+      lq = lq_c[0], lk = lk_c[0];
+#pragma unroll
+      for (int i = 1; i < kCached; i++)
+        if (c == i) lq = lq_c[i], lk = lk_c[i];
+    } else {
+      lq = lk = 0;
+      if (c * 64 + lane < n_seqs) sizes(c * 64 + lane, lq, lk);
+    }
+  };
+  // items of one sequence whose weight is at least w
+  auto count_s = [&](int lq, int lk, int w) -> int {
+    const int n = (lq + BM - 1) / BM;
+    if (w <= 0) return n;
+    const int x = (w - 1) * BN;  // W >= w  <=>  the streamed keys exceed x
+    if (lk <= x) return 0;
+    if (!CAUSAL) return n;
+    const int t = x - (lk - lq);  // need min((qt + 1) BM, Lq) > t
+    if (lq <= t) return 0;
+    return n - (t < 0 ? 0 : t / BM);
+  };
+  const int chunks = (n_seqs + 63) / 64;
+  auto count = [&](int w) -> int {
+    int c_sum = 0;
+    for (int c = 0; c < chunks; c++) {
+      int lq, lk;
+      get(c, lq, lk);
+      c_sum += count_s(lq, lk, w);
+    }
+    return wave_sum(c_sum);
+  };
+  const int total = count(0);
+  if (rank >= total * a.Hq) return false;
+  // the largest w whose items (times heads) outnumber rank
+  int lo = 0, hi = a.Nk / BN + 2;  // count(hi) == 0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count(mid) * a.Hq > rank) lo = mid;
+    else hi = mid;
+  }
+  const int r2 = rank - count(lo + 1) * a.Hq;  // index among the items of weight exactly lo
+  const int u = r2 / a.Hq, j = r2 % a.Hq;
+  int before = 0;
+  for (int c = 0; c < chunks; c++) {
+    int lq, lk;
+    get(c, lq, lk);
+    const int cw = count_s(lq, lk, lo);
+    const int e = cw - count_s(lq, lk, lo + 1);
+    const int incl = wave_incl_scan(e, lane);
+    const int excl = incl - e;
+    const bool hit = e > 0 && before + excl <= u && u < before + incl;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+    if (m != 0) {
+      const int src = (int)__builtin_ctzll(m);
+      const int n = (lq + BM - 1) / BM;
+      s_out = c * 64 + src;
+      qt_out = __builtin_amdgcn_readlane(n - cw + (u - before - excl), src);
+      const int g = a.Hq / a.Hkv;
+      h_out = (j % a.Hkv) * g + j / a.Hkv;
+      return true;
+    }
+    before += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return false;  // not reached: the counts above place every rank
+}
+
 template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = NW * 32;
@@ -105,20 +225,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- work decomposition: (b, kv head) pair, then q tile (descending when
-  // causal) and head in group
-  // A packed batch's sequences differ in length, so the XCD-local order
-  // (which gives each XCD whole sequences) would leave some XCDs with far
-  // more work than others: there every XCD gets a share of every sequence.
-  const WorkItem wi = (a.cu_q != nullptr)
-                          ? WorkItem{(int)(blockIdx.x % (a.B * a.Hkv)), (int)(blockIdx.x / (a.B * a.Hkv))}
-                          : lpt_order(snake_pid(blockIdx.x, a.n_wgs, a.snake), a.B * a.Hkv, a.g * a.n_qtiles);
-  const int pair = wi.pair;
-  const int rem = wi.sub;
-  const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
-  const int hq = (pair % a.Hkv) * a.g + rem % a.g;
-  const int b = pair / a.Hkv;
-  const int kvh = pair % a.Hkv;
+  // ---- work decomposition.  Dense: (b, kv head) pair, then q tile
+  // (descending when causal) and head in group.  Packed batch: the
+  // sequences differ in length, so the launch order follows each item's
+  // own weight, longest first (varlen_item).
+  int qt, hq, b, kvh;
+  if (a.cu_q != nullptr) {
+    if (!varlen_item<BM, BN, CAUSAL, PAGED>(a, (int)blockIdx.x, b, qt, hq)) return;
+    kvh = hq / a.g;
+  } else {
+    const WorkItem wi = lpt_order(snake_pid(blockIdx.x, a.n_wgs, a.snake), a.B * a.Hkv, a.g * a.n_qtiles);
+    const int rem = wi.sub;
+    qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
+    hq = (wi.pair % a.Hkv) * a.g + rem % a.g;
+    b = wi.pair / a.Hkv;
+    kvh = wi.pair % a.Hkv;
+  }
 
   const int i0 = qt * BM;
   const int qw0 = i0 + wave * 32;
