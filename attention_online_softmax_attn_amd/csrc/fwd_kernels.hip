@@ -618,6 +618,299 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgsF32 a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense forward in two alternating wave groups (8 waves, 256 query rows).
+// Per 64-key tile a wave has 32 MFMAs (S^T = K Q^T and O^T += V^T P^T) and
+// the softmax between them, ~3.5 VALU instructions per MFMA, one of them an
+// exponential.  A SIMD hosts one wave of each group (waves w and w + 4), and
+// the groups run in anti-phase, separated by a workgroup barrier at every
+// phase boundary: while one wave of a SIMD issues only MFMAs (the P V of the
+// previous tile and the S^T of this one), its partner issues only the VALU
+// work of its softmax, so the exponentials of one wave execute under the
+// contractions of the other instead of after them.  Per tile and group:
+//
+//   MFMA phase (tile t):  O^T += V(t-1)^T P(t-1)^T,  S^T(t) = K(t) Q^T
+//   VALU phase (tile t):  mask, online softmax of S^T(t) -> P(t)
+//
+// Group 0 runs MFMA(t) in phase 2t and VALU(t) in phase 2t + 1; group 1 one
+// phase later.  K(t) and V(t - 1) are read in phases 2t (group 0) and 2t + 1
+// (group 1); at the start of phase 2t the workgroup loads K(t + 1) and V(t)
+// into the buffers K(t - 1) and V(t - 2) left, which must land before phase
+// 2t + 2: the wait before that phase's barrier covers them, so the loads
+// have two phases to arrive.  Results are the same bits as fwd_bf16_kernel:
+// the per-tile arithmetic and its order are unchanged, only the interleaving
+// of the two groups differs.
+//
+// ATTN_FWD_PP_GROUPS 1: the MFMA phase's operand reads are scheduled two
+// contractions ahead of their MFMAs (scheduling groups; the compiler's own
+// order measured 3-8 % slower)
+#ifndef ATTN_FWD_PP_GROUPS
+#define ATTN_FWD_PP_GROUPS 1
+#endif
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
+  constexpr int NW = 8, BM = NW * 32, BN = 64, KB = 2;
+  constexpr int TILE_BYTES = BN * D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = BN * CPR / (64 * NW);
+  static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly over the workgroup");
+  __shared__ __attribute__((aligned(1024))) char k_st0[TILE_BYTES], k_st1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_st0[TILE_BYTES], v_st1[TILE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
+  const int h32 = lane >> 5;
+  const int l32 = lane & 31;
+
+  const WorkItem wi = lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_qtiles);
+  const int rem = wi.sub;
+  const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
+  const int hq = (wi.pair % a.Hkv) * a.g + rem % a.g;
+  const int b = wi.pair / a.Hkv;
+  const int kvh = wi.pair % a.Hkv;
+  const int i0 = qt * BM;
+  const int qw0 = i0 + wave * 32;
+  const int Nq = a.Nq, Nk = a.Nk;
+  const size_t q_head = ((size_t)b * a.Hq + hq) * (size_t)Nq * D;
+  const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)Nk * D;
+  const size_t lse_row = ((size_t)b * a.Hq + hq) * (size_t)Nq;
+  const int off = Nk - Nq;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_head, (uint32_t)Nq * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)Nk * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head, (uint32_t)Nk * D * 2);
+  int kend = Nk;
+  if (CAUSAL) kend = min(Nk, min(i0 + BM, Nq) - 1 + off + 1);
+  const int n = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  auto issue1 = [&](int t, char* dst, __amdgpu_buffer_rsrc_t r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < LOADS; m++) {
+      const int slab = m * NW + wave;
+      const int p = slab * 64 + lane;
+      const int row = p / CPR;
+      const int c = (p % CPR) ^ swz<D>(row);
+      buf_load_lds16(r, (uint32_t)(((t * BN + row) * D + c * 8) * 2), (lds_void*)(dst + slab * 1024));
+    }
+  };
+  if (n > 0) issue1(0, k_st0, rk);
+
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; s++)
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(((qw0 + l32) * D + 16 * s + 8 * h32) * 2)));
+
+  const int swl = swz<D>(l32);
+  int koff[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; s++) koff[s] = l32 * (D * 2) + (((2 * s + h32) ^ swl) << 4);
+  int voff[D / 32][2];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+    for (int lh = 0; lh < 2; lh++)
+      voff[cb][lh] = tile_off<D>(4 * h32 + ((lane & 15) >> 2) + 8 * lh, cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++) acc[cb] = f32x16{};
+  float m_run = kNegInf, l_run = 0.0f;
+  const int qi = qw0 + l32;
+  f32x16 st[KB];      // S^T of the tile between its MFMA and VALU phases
+  bf16x8 pb[KB][2];   // P of the tile between its VALU phase and the next MFMA phase
+
+  auto visible = [&](int t) __attribute__((always_inline)) {
+    return t >= 0 && t < n && (!CAUSAL || t * BN <= qw0 + 31 + off);
+  };
+  // MFMA phase of tile t: P V of tile t - 1 (V in vp), S^T of tile t (K in kc)
+  auto mfma_phase = [&](int t, const char* __restrict__ kc, const char* __restrict__ vp)
+                        __attribute__((always_inline)) {
+    if (visible(t - 1)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+          const char* vk = vp + (kb * 32 + 16 * hf) * (D * 2);
+#pragma unroll
+          for (int cb = 0; cb < D / 32; cb++) {
+            const s16x4 lo = ds_read_tr16(vk + voff[cb][0]);
+            const s16x4 hi = ds_read_tr16(vk + voff[cb][1]);
+            acc[cb] = mfma32(join_bf16(lo, hi), pb[kb][hf], acc[cb]);
+          }
+        }
+#if ATTN_FWD_PP_GROUPS
+      // operand reads run two contractions ahead of their MFMAs, not all
+      // hoisted to the top (which would hold 64 more registers)
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KB * (D / 32) - 3; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+#endif
+    }
+    // P dies before S^T is born: the two never hold registers at once
+    __builtin_amdgcn_sched_barrier(0);
+    if (visible(t)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++) st[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < D / 16; s++)
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++)
+          st[kb] = mfma32(*(const bf16x8*)(kc + koff[s] + kb * 32 * (D * 2)), qf[s], st[kb]);
+#if ATTN_FWD_PP_GROUPS
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int i = 0; i < KB * (D / 16) - 3; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+#endif
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // VALU phase of tile t: the online softmax of fwd_bf16_kernel, on st -> pb
+  auto valu_phase = [&](int t) __attribute__((always_inline)) {
+    if (!visible(t)) return;
+    const int j0 = t * BN;
+    bool need_mask = (j0 + BN > Nk);
+    if (CAUSAL && j0 + BN - 1 > qw0 + off) need_mask = true;
+    if (need_mask) {
+      const int lim = (CAUSAL ? min(Nk, qi + off + 1) : Nk) - j0 - 4 * h32;
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if (!(kb * 32 + 8 * (r >> 2) + (r & 3) < lim)) st[kb][r] = kNegInf;
+    }
+    float psum = 0.0f;
+    bool fast = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
+    if (fast) {
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float p = fast_exp2(__builtin_fmaf(st[kb][8 * hf + e], a.c, -m_run));
+            pb[kb][hf][e] = to_bf16(p);
+            psum += p;
+          }
+      fast = __builtin_amdgcn_ballot_w64(!(psum <= 65536.0f)) == 0;
+    }
+    if (!fast) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[kb][r]);
+      mx = halves_max(mx) * a.c;
+      const bool grow = mx > m_run + kTau;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? fast_exp2(m_run - mx) : 1.0f;
+        m_run = grow ? mx : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) acc[cb][r] *= alpha;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+      psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float p = fast_exp2(__builtin_fmaf(st[kb][8 * hf + e], a.c, -m_use));
+            pb[kb][hf][e] = to_bf16(p);
+            psum += p;
+          }
+    }
+    l_run += psum;
+  };
+  // phases 2t and 2t + 1 of tile t; kc, vp: K(t) and V(t - 1); kf, vf: the
+  // buffers K(t + 1) and V(t) are loaded into.  Each group runs its own loop
+  // (the same barriers in the same number), so that the register allocator
+  // sees one group's phase order at a time.
+  auto start = [&](int t, char* __restrict__ kf, char* __restrict__ vf) __attribute__((always_inline)) {
+    // phase 2t: the loads of phase 2t - 2 (K(t), V(t - 1)) have landed and
+    // every wave is done with K(t - 1) and V(t - 2)
+    wait_vmem();
+    barrier_nofence();
+    if (t + 1 < n) issue1(t + 1, kf, rk);
+    if (t < n) issue1(t, vf, rv);
+  };
+  if (grp == 0) {
+    auto tile = [&](int t, const char* __restrict__ kc, const char* __restrict__ vp, char* __restrict__ kf,
+                    char* __restrict__ vf) __attribute__((always_inline)) {
+      start(t, kf, vf);
+      mfma_phase(t, kc, vp);
+      barrier_nofence();  // phase 2t + 1 (the loads just issued stay in flight)
+      valu_phase(t);
+    };
+    for (int t = 0; t <= n; t += 2) {
+      tile(t, k_st0, v_st1, k_st1, v_st0);
+      if (t + 1 > n) break;
+      tile(t + 1, k_st1, v_st0, k_st0, v_st1);
+    }
+  } else {
+    auto tile = [&](int t, const char* __restrict__ kc, const char* __restrict__ vp, char* __restrict__ kf,
+                    char* __restrict__ vf) __attribute__((always_inline)) {
+      start(t, kf, vf);
+      valu_phase(t - 1);
+      barrier_nofence();
+      mfma_phase(t, kc, vp);
+    };
+    for (int t = 0; t <= n; t += 2) {
+      tile(t, k_st0, v_st1, k_st1, v_st0);
+      if (t + 1 > n) break;
+      tile(t + 1, k_st1, v_st0, k_st0, v_st1);
+    }
+  }
+
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qi < Nq) {
+    __bf16* orow = a.o + q_head + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; e++) w[e] = to_bf16(acc[cb][4 * g4 + e] * inv);
+        *(bf16x4*)(orow + cb * 32 + 8 * g4 + 4 * h32) = w;
+      }
+    if (a.lse != nullptr && h32 == 0) a.lse[lse_row + qi] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_pp(const FwdProblem& p, hipStream_t s) {
+  FwdArgs a{};
+  a.q = (const __bf16*)p.q;
+  a.k = (const __bf16*)p.k;
+  a.v = (const __bf16*)p.v;
+  a.o = (__bf16*)p.o;
+  a.lse = p.lse;
+  a.B = (int)p.B;
+  a.Hq = (int)p.Hq;
+  a.Hkv = (int)p.Hkv;
+  a.Nq = (int)p.Nq;
+  a.Nk = (int)p.Nk;
+  a.g = a.Hq / a.Hkv;
+  a.n_qtiles = (a.Nq + 255) / 256;
+  a.n_wgs = a.B * a.Hq * a.n_qtiles;
+  a.c = p.scale * kLog2e;
+  hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL>), dim3(a.n_wgs), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 hipError_t launch_bf16(const FwdProblem& p, hipStream_t s) {
   FwdArgs a;
@@ -678,13 +971,21 @@ hipError_t launch_f32(const FwdProblem& p, hipStream_t s) {
 #ifndef ATTN_FWD_BIG_BN
 #define ATTN_FWD_BIG_BN 64
 #endif
+// 1: dense problems with 8-wave workgroups run the two-group kernel
+#ifndef ATTN_FWD_PP
+#define ATTN_FWD_PP 1
+#endif
+// packed batches take 8-wave workgroups from this many 256-row tiles
+#ifndef ATTN_FWD_PACKED_MIN_BIG
+#define ATTN_FWD_PACKED_MIN_BIG (8 * 256)
+#endif
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
   const bool causal = p.causal != 0;
   if (p.paged) {
     // packed batch over a paged K/V cache (bf16)
     constexpr int NWB = ATTN_FWD_BIG_NW, BNB = ATTN_FWD_BIG_BN;
-    const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= 8 * 256;
+    const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= ATTN_FWD_PACKED_MIN_BIG;
     if (p.d == 128) {
       if (big)
         return causal ? launch_bf16<128, NWB, BNB, true, true>(p, s) : launch_bf16<128, NWB, BNB, false, true>(p, s);
@@ -704,8 +1005,12 @@ hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
     // the longest one's length, keep 4 waves up to 8 per CU (8 waves measured
     // 9 % slower on 4 sequences of 600..2048 tokens, equal on 8).
     constexpr int NWB = ATTN_FWD_BIG_NW, BNB = ATTN_FWD_BIG_BN;
-    const int64_t min_big = p.cu_q != nullptr ? 8 * 256 : 2 * 256;
+    const int64_t min_big = p.cu_q != nullptr ? ATTN_FWD_PACKED_MIN_BIG : 2 * 256;
     const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= min_big;
+    if (ATTN_FWD_PP && big && p.cu_q == nullptr) {
+      if (p.d == 128) return causal ? launch_pp<128, true>(p, s) : launch_pp<128, false>(p, s);
+      return causal ? launch_pp<64, true>(p, s) : launch_pp<64, false>(p, s);
+    }
     if (p.d == 128) {
       if (big) return causal ? launch_bf16<128, NWB, BNB, true>(p, s) : launch_bf16<128, NWB, BNB, false>(p, s);
       return causal ? launch_bf16<128, 4, 64, true>(p, s) : launch_bf16<128, 4, 64, false>(p, s);
