@@ -634,12 +634,14 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgsF32 a) {
 //
 // Group 0 runs MFMA(t) in phase 2t and VALU(t) in phase 2t + 1; group 1 one
 // phase later.  K(t) and V(t - 1) are read in phases 2t (group 0) and 2t + 1
-// (group 1); at the start of phase 2t the workgroup loads K(t + 1) and V(t)
-// into the buffers K(t - 1) and V(t - 2) left, which must land before phase
-// 2t + 2: the wait before that phase's barrier covers them, so the loads
-// have two phases to arrive.  Results are the same bits as fwd_bf16_kernel:
-// the per-tile arithmetic and its order are unchanged, only the interleaving
-// of the two groups differs.
+// (group 1).  The loads are issued by the group entering its VALU phase, so
+// that the group entering its MFMA phase starts its contractions at once
+// (all eight waves issuing at the phase start held the MFMA group ~650
+// cycles): group 1 loads K(t + 1) at the start of phase 2t and group 0 loads
+// V(t + 1) at the start of phase 2t + 1, each into the buffer the tile three
+// before it left (three K and three V buffers).  Results are the same bits
+// as fwd_bf16_kernel: the per-tile arithmetic and its order are unchanged,
+// only the interleaving of the two groups differs.
 //
 // ATTN_FWD_PP_GROUPS 1: the MFMA phase's operand reads are scheduled two
 // contractions ahead of their MFMAs (scheduling groups; the compiler's own
@@ -654,8 +656,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   constexpr int CPR = D / 8;
   constexpr int LOADS = BN * CPR / (64 * NW);
   static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly over the workgroup");
-  __shared__ __attribute__((aligned(1024))) char k_st0[TILE_BYTES], k_st1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v_st0[TILE_BYTES], v_st1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_st0[TILE_BYTES], k_st1[TILE_BYTES], k_st2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_st0[TILE_BYTES], v_st1[TILE_BYTES], v_st2[TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -693,12 +695,27 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       buf_load_lds16(r, (uint32_t)(((t * BN + row) * D + c * 8) * 2), (lds_void*)(dst + slab * 1024));
     }
   };
+  // a K (or V) tile loaded by the four waves of one group
+  auto issue4 = [&](int t, char* dst, __amdgpu_buffer_rsrc_t r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 2 * LOADS; m++) {
+      const int slab = m * (NW / 2) + (wave & 3);
+      const int p = slab * 64 + lane;
+      const int row = p / CPR;
+      const int c = (p % CPR) ^ swz<D>(row);
+      buf_load_lds16(r, (uint32_t)(((t * BN + row) * D + c * 8) * 2), (lds_void*)(dst + slab * 1024));
+    }
+  };
   if (n > 0) issue1(0, k_st0, rk);
+  if (n > 0 && grp == 0) issue4(0, v_st0, rv);
 
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; s++)
     qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(((qw0 + l32) * D + 16 * s + 8 * h32) * 2)));
+  // Q, K(0) and V(0) complete here, so that no later counted wait has to
+  // cover the Q registers
+  wait_vmem();
 
   const int swl = swz<D>(l32);
   int koff[D / 16];
@@ -833,43 +850,51 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
     l_run += psum;
   };
-  // phases 2t and 2t + 1 of tile t; kc, vp: K(t) and V(t - 1); kf, vf: the
-  // buffers K(t + 1) and V(t) are loaded into.  Each group runs its own loop
-  // (the same barriers in the same number), so that the register allocator
-  // sees one group's phase order at a time.
-  auto start = [&](int t, char* __restrict__ kf, char* __restrict__ vf) __attribute__((always_inline)) {
-    // phase 2t: the loads of phase 2t - 2 (K(t), V(t - 1)) have landed and
-    // every wave is done with K(t - 1) and V(t - 2)
-    wait_vmem();
-    barrier_nofence();
-    if (t + 1 < n) issue1(t + 1, kf, rk);
-    if (t < n) issue1(t, vf, rv);
-  };
+  // Tile t takes phases 2t and 2t + 1.  Each group loads in its VALU
+  // phases, so that the MFMA group never waits to issue loads: group 1
+  // issues K(t + 1) at the start of phase 2t (needed at phase 2t + 2) and
+  // group 0 issues V(t + 1) at the start of phase 2t + 1 (needed at phase
+  // 2t + 4), each into the buffer the tile three before it left.  At the
+  // start of phase 2t group 1 waits for all its loads (K(t)) and group 0 for
+  // all but V(t) (so V(t - 1) has landed), then the barrier publishes them.
+  // Each group runs its own loop (the same barriers in the same number), so
+  // that the register allocator sees one group's phase order at a time.
   if (grp == 0) {
-    auto tile = [&](int t, const char* __restrict__ kc, const char* __restrict__ vp, char* __restrict__ kf,
-                    char* __restrict__ vf) __attribute__((always_inline)) {
-      start(t, kf, vf);
+    auto tile = [&](int t, const char* __restrict__ kc, const char* __restrict__ vp, char* __restrict__ vn)
+                    __attribute__((always_inline)) {
+      if (t >= 1 && t < n)
+        wait_vmem_n<2 * LOADS>();  // V(t) may still be in flight
+      else
+        wait_vmem();
+      barrier_nofence();  // phase 2t
       mfma_phase(t, kc, vp);
-      barrier_nofence();  // phase 2t + 1 (the loads just issued stay in flight)
+      barrier_nofence();  // phase 2t + 1
+      if (t + 1 < n) issue4(t + 1, vn, rv);
       valu_phase(t);
     };
-    for (int t = 0; t <= n; t += 2) {
-      tile(t, k_st0, v_st1, k_st1, v_st0);
+    for (int t = 0; t <= n; t += 3) {
+      tile(t, k_st0, v_st2, v_st1);
       if (t + 1 > n) break;
-      tile(t + 1, k_st1, v_st0, k_st0, v_st1);
+      tile(t + 1, k_st1, v_st0, v_st2);
+      if (t + 2 > n) break;
+      tile(t + 2, k_st2, v_st1, v_st0);
     }
   } else {
-    auto tile = [&](int t, const char* __restrict__ kc, const char* __restrict__ vp, char* __restrict__ kf,
-                    char* __restrict__ vf) __attribute__((always_inline)) {
-      start(t, kf, vf);
+    auto tile = [&](int t, const char* __restrict__ kc, const char* __restrict__ vp, char* __restrict__ kn)
+                    __attribute__((always_inline)) {
+      wait_vmem();
+      barrier_nofence();  // phase 2t
+      if (t + 1 < n) issue4(t + 1, kn, rk);
       valu_phase(t - 1);
-      barrier_nofence();
+      barrier_nofence();  // phase 2t + 1
       mfma_phase(t, kc, vp);
     };
-    for (int t = 0; t <= n; t += 2) {
-      tile(t, k_st0, v_st1, k_st1, v_st0);
+    for (int t = 0; t <= n; t += 3) {
+      tile(t, k_st0, v_st2, k_st1);
       if (t + 1 > n) break;
-      tile(t + 1, k_st1, v_st0, k_st0, v_st1);
+      tile(t + 1, k_st1, v_st0, k_st2);
+      if (t + 2 > n) break;
+      tile(t + 2, k_st2, v_st1, k_st0);
     }
   }
 
