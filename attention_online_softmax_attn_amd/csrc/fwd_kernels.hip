@@ -649,13 +649,14 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgsF32 a) {
 #ifndef ATTN_FWD_PP_GROUPS
 #define ATTN_FWD_PP_GROUPS 1
 #endif
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN = false, bool PAGED = false>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   constexpr int NW = 8, BM = NW * 32, BN = 64, KB = 2;
   constexpr int TILE_BYTES = BN * D * 2;
   constexpr int CPR = D / 8;
   constexpr int LOADS = BN * CPR / (64 * NW);
   static_assert(LOADS * 64 * NW == BN * CPR, "tile must split evenly over the workgroup");
+  static_assert(!PAGED || VARLEN, "the paged layout comes with a packed batch");
   __shared__ __attribute__((aligned(1024))) char k_st0[TILE_BYTES], k_st1[TILE_BYTES], k_st2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_st0[TILE_BYTES], v_st1[TILE_BYTES], v_st2[TILE_BYTES];
 
@@ -665,18 +666,44 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
-  const WorkItem wi = lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_qtiles);
-  const int rem = wi.sub;
-  const int qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
-  const int hq = (wi.pair % a.Hkv) * a.g + rem % a.g;
-  const int b = wi.pair / a.Hkv;
-  const int kvh = wi.pair % a.Hkv;
+  // work item and this (batch or sequence, head) slice, as in fwd_bf16_kernel
+  int qt, hq, b, kvh;
+  if constexpr (VARLEN) {
+    if (!varlen_item<BM, BN, CAUSAL, PAGED>(a, (int)blockIdx.x, b, qt, hq)) return;
+    kvh = hq / a.g;
+  } else {
+    const WorkItem wi = lpt_order(blockIdx.x, a.B * a.Hkv, a.g * a.n_qtiles);
+    const int rem = wi.sub;
+    qt = CAUSAL ? (a.n_qtiles - 1 - rem / a.g) : (rem / a.g);
+    hq = (wi.pair % a.Hkv) * a.g + rem % a.g;
+    b = wi.pair / a.Hkv;
+    kvh = wi.pair % a.Hkv;
+  }
   const int i0 = qt * BM;
   const int qw0 = i0 + wave * 32;
-  const int Nq = a.Nq, Nk = a.Nk;
-  const size_t q_head = ((size_t)b * a.Hq + hq) * (size_t)Nq * D;
-  const size_t kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)Nk * D;
-  const size_t lse_row = ((size_t)b * a.Hq + hq) * (size_t)Nq;
+  int Nq = a.Nq, Nk = a.Nk;
+  size_t q_head, kv_head, lse_row;
+  if constexpr (VARLEN) {
+    // clamped, so that offsets that do not describe a packed batch cannot
+    // take a load outside q, k or v
+    const int q1 = min(a.cu_q[b + 1], a.tot_q), q0 = max(0, min(a.cu_q[b], q1));
+    Nq = q1 - q0;
+    q_head = ((size_t)hq * a.tot_q + q0) * D;
+    lse_row = (size_t)hq * a.tot_q + q0;
+    if constexpr (PAGED) {
+      Nk = min(max(a.seq_lens_k[b], 0), min(a.Nk, a.max_pages * a.page));
+      kv_head = 0;
+    } else {
+      const int k1 = min(a.cu_k[b + 1], a.tot_k), k0 = max(0, min(a.cu_k[b], k1));
+      Nk = k1 - k0;
+      kv_head = ((size_t)kvh * a.tot_k + k0) * D;
+    }
+    if (i0 >= Nq) return;  // the whole workgroup: a tile past this sequence's queries
+  } else {
+    q_head = ((size_t)b * a.Hq + hq) * (size_t)Nq * D;
+    kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)Nk * D;
+    lse_row = ((size_t)b * a.Hq + hq) * (size_t)Nq;
+  }
   const int off = Nk - Nq;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_head, (uint32_t)Nq * D * 2);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)Nk * D * 2);
@@ -685,29 +712,56 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   if (CAUSAL) kend = min(Nk, min(i0 + BM, Nq) - 1 + off + 1);
   const int n = kend > 0 ? (kend + BN - 1) / BN : 0;
 
-  auto issue1 = [&](int t, char* dst, __amdgpu_buffer_rsrc_t r) __attribute__((always_inline)) {
+  // paged: the page ids of the first 64 pages, one per lane
+  int pg_lane = 0;
+  if constexpr (PAGED) {
+    if (lane < (kend + a.page - 1) / a.page) pg_lane = a.block_table[(size_t)b * a.max_pages + lane];
+  }
+  // the buffer and first row that tile t of K (or V) is loaded from; a paged
+  // tile lies in one page (pages are whole multiples of 64 keys), rows past
+  // the sequence's keys read as zeros and a page id outside the cache is
+  // clamped into it
+  auto tile_src = [&](int t, bool is_v, int& row0) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      const int j0 = t * BN;
+      const int pi = j0 / a.page;
+      const int id = pi < 64 ? __builtin_amdgcn_readlane(pg_lane, pi) : a.block_table[(size_t)b * a.max_pages + pi];
+      const int pg = min(max(id, 0), a.num_pages - 1);
+      const size_t base = (((size_t)pg * a.Hkv + kvh) * a.page + (j0 % a.page)) * D;
+      row0 = 0;
+      return make_rsrc((is_v ? a.v : a.k) + base, (uint32_t)min(BN, Nk - j0) * D * 2);
+    } else {
+      row0 = t * BN;
+      return is_v ? rv : rk;
+    }
+  };
+  auto issue1 = [&](int t, char* dst, bool is_v) __attribute__((always_inline)) {
+    int row0;
+    const __amdgpu_buffer_rsrc_t r = tile_src(t, is_v, row0);
 #pragma unroll
     for (int m = 0; m < LOADS; m++) {
       const int slab = m * NW + wave;
       const int p = slab * 64 + lane;
       const int row = p / CPR;
       const int c = (p % CPR) ^ swz<D>(row);
-      buf_load_lds16(r, (uint32_t)(((t * BN + row) * D + c * 8) * 2), (lds_void*)(dst + slab * 1024));
+      buf_load_lds16(r, (uint32_t)(((row0 + row) * D + c * 8) * 2), (lds_void*)(dst + slab * 1024));
     }
   };
   // a K (or V) tile loaded by the four waves of one group
-  auto issue4 = [&](int t, char* dst, __amdgpu_buffer_rsrc_t r) __attribute__((always_inline)) {
+  auto issue4 = [&](int t, char* dst, bool is_v) __attribute__((always_inline)) {
+    int row0;
+    const __amdgpu_buffer_rsrc_t r = tile_src(t, is_v, row0);
 #pragma unroll
     for (int m = 0; m < 2 * LOADS; m++) {
       const int slab = m * (NW / 2) + (wave & 3);
       const int p = slab * 64 + lane;
       const int row = p / CPR;
       const int c = (p % CPR) ^ swz<D>(row);
-      buf_load_lds16(r, (uint32_t)(((t * BN + row) * D + c * 8) * 2), (lds_void*)(dst + slab * 1024));
+      buf_load_lds16(r, (uint32_t)(((row0 + row) * D + c * 8) * 2), (lds_void*)(dst + slab * 1024));
     }
   };
-  if (n > 0) issue1(0, k_st0, rk);
-  if (n > 0 && grp == 0) issue4(0, v_st0, rv);
+  if (n > 0) issue1(0, k_st0, false);
+  if (n > 0 && grp == 0) issue4(0, v_st0, true);
 
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -869,7 +923,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       barrier_nofence();  // phase 2t
       mfma_phase(t, kc, vp);
       barrier_nofence();  // phase 2t + 1
-      if (t + 1 < n) issue4(t + 1, vn, rv);
+      if (t + 1 < n) issue4(t + 1, vn, true);
       valu_phase(t);
     };
     for (int t = 0; t <= n; t += 3) {
@@ -884,7 +938,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
                     __attribute__((always_inline)) {
       wait_vmem();
       barrier_nofence();  // phase 2t
-      if (t + 1 < n) issue4(t + 1, kn, rk);
+      if (t + 1 < n) issue4(t + 1, kn, false);
       valu_phase(t - 1);
       barrier_nofence();  // phase 2t + 1
       mfma_phase(t, kc, vp);
@@ -915,7 +969,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN = false, bool PAGED = false>
 hipError_t launch_pp(const FwdProblem& p, hipStream_t s) {
   FwdArgs a{};
   a.q = (const __bf16*)p.q;
@@ -932,7 +986,16 @@ hipError_t launch_pp(const FwdProblem& p, hipStream_t s) {
   a.n_qtiles = (a.Nq + 255) / 256;
   a.n_wgs = a.B * a.Hq * a.n_qtiles;
   a.c = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL>), dim3(a.n_wgs), dim3(512), 0, s, a);
+  a.cu_q = p.cu_q;
+  a.cu_k = p.cu_k;
+  a.tot_q = (int)p.tot_q;
+  a.tot_k = (int)p.tot_k;
+  a.block_table = p.block_table;
+  a.seq_lens_k = p.seq_lens_k;
+  a.page = (int)p.page;
+  a.max_pages = (int)p.max_pages;
+  a.num_pages = (int)p.num_pages;
+  hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, VARLEN, PAGED>), dim3(a.n_wgs), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1011,6 +1074,10 @@ hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
     // packed batch over a paged K/V cache (bf16)
     constexpr int NWB = ATTN_FWD_BIG_NW, BNB = ATTN_FWD_BIG_BN;
     const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= ATTN_FWD_PACKED_MIN_BIG;
+    if (ATTN_FWD_PP && big) {
+      if (p.d == 128) return causal ? launch_pp<128, true, true, true>(p, s) : launch_pp<128, false, true, true>(p, s);
+      return causal ? launch_pp<64, true, true, true>(p, s) : launch_pp<64, false, true, true>(p, s);
+    }
     if (p.d == 128) {
       if (big)
         return causal ? launch_bf16<128, NWB, BNB, true, true>(p, s) : launch_bf16<128, NWB, BNB, false, true>(p, s);
@@ -1035,6 +1102,10 @@ hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
     if (ATTN_FWD_PP && big && p.cu_q == nullptr) {
       if (p.d == 128) return causal ? launch_pp<128, true>(p, s) : launch_pp<128, false>(p, s);
       return causal ? launch_pp<64, true>(p, s) : launch_pp<64, false>(p, s);
+    }
+    if (ATTN_FWD_PP && big) {
+      if (p.d == 128) return causal ? launch_pp<128, true, true>(p, s) : launch_pp<128, false, true>(p, s);
+      return causal ? launch_pp<64, true, true>(p, s) : launch_pp<64, false, true>(p, s);
     }
     if (p.d == 128) {
       if (big) return causal ? launch_bf16<128, NWB, BNB, true>(p, s) : launch_bf16<128, NWB, BNB, false>(p, s);

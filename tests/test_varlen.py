@@ -11,7 +11,8 @@ CPU: the oracle's packed-batch composition is pinned to a 50-digit brute
 force that reads sequence membership straight off the packed rows.
 GPU: attn_fwd_varlen against that oracle on every row of small batches
 (ragged lengths across tile boundaries, empty sequences, Lq < Lk and
-Lq > Lk, grouped-query heads, d = 64 and 128), against the dense entry point
+Lq > Lk, grouped-query heads, d = 64 and 128; two of them large enough in
+tiles for the two-group kernel), against the dense entry point
 when every sequence has the same length, and on sampled rows of a large
 chunked-prefill batch.
 """
@@ -73,6 +74,21 @@ SMALL = [
     ([40, 200, 17], [20, 60, 0], 2, 1, 128),                 # Lq > Lk and a sequence with no keys
     ([300, 1, 129], [700, 513, 129], 8, 2, 64),
 ]
+
+
+# Packed batches of at least 2048 tiles of 256 rows (every sequence counted at
+# the longest one's length) take the two-group 8-wave kernel: here one
+# 1100-row sequence gives 16 x 32 x 5 = 2560 such tiles, and the other
+# sequences are short, ragged, empty or without keys, so that every row can
+# be checked against the oracle.
+TWO_GROUP_LQ = [1100, 37, 300, 5, 256, 257, 0, 64, 129, 700, 1, 90, 255, 513, 31, 200]
+TWO_GROUP_LK = [1300, 37, 400, 5, 256, 900, 0, 64, 129, 700, 300, 90, 255, 513, 31, 0]
+SMALL += [(TWO_GROUP_LQ, TWO_GROUP_LK, 32, 8, 128), (TWO_GROUP_LQ, TWO_GROUP_LK, 32, 8, 64)]
+
+
+def test_two_group_cases_reach_the_packed_threshold():
+    for lens_q, _, Hq, _, _ in SMALL[-2:]:
+        assert len(lens_q) * Hq * -(-max(lens_q) // 256) >= 2048
 
 
 @pytest.mark.gpu

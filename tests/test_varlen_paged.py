@@ -56,6 +56,11 @@ CASES = [
     ([40, 200, 17, 0], [20, 60, 0, 5], 2, 1, 128, 128),          # Lq > Lk, a sequence with no keys
     ([300, 1, 129], [700, 513, 129], 8, 2, 256, 128),
     ([65, 64, 63], [65, 64, 63], 4, 2, 64, 128),                  # prefill from an empty cache
+    # 16 x 32 x 5 tiles of 256 rows: the two-group 8-wave kernel; the longest
+    # history spans more than 64 pages of 64 keys (the page-table path past
+    # the per-lane copy)
+    ([1100, 37, 300, 5, 256, 257, 0, 64, 129, 700, 1, 90, 255, 513, 31, 200],
+     [4300, 37, 400, 5, 256, 900, 0, 64, 129, 700, 300, 90, 255, 513, 31, 0], 32, 8, 64, 128),
 ]
 
 
