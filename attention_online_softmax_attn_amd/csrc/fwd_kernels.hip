@@ -1063,6 +1063,11 @@ hipError_t launch_f32(const FwdProblem& p, hipStream_t s) {
 #ifndef ATTN_FWD_PP
 #define ATTN_FWD_PP 1
 #endif
+// causal dense problems take 8-wave workgroups from this many 256-row tiles
+// (non-causal ones from half as many)
+#ifndef ATTN_FWD_DENSE_MIN_BIG
+#define ATTN_FWD_DENSE_MIN_BIG (2 * 256)
+#endif
 // packed batches take 8-wave workgroups from this many 256-row tiles
 #ifndef ATTN_FWD_PACKED_MIN_BIG
 #define ATTN_FWD_PACKED_MIN_BIG (8 * 256)
@@ -1097,7 +1102,12 @@ hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
     // the longest one's length, keep 4 waves up to 8 per CU (8 waves measured
     // 9 % slower on 4 sequences of 600..2048 tokens, equal on 8).
     constexpr int NWB = ATTN_FWD_BIG_NW, BNB = ATTN_FWD_BIG_BN;
-    const int64_t min_big = p.cu_q != nullptr ? ATTN_FWD_PACKED_MIN_BIG : 2 * 256;
+    // a non-causal grid of equal workgroups fills the machine with one
+    // two-group workgroup per CU (10 % faster at N = 2048, 32 heads, 256
+    // such tiles); causal ones, whose workgroups differ up to 16-fold, need
+    // two per CU over the launch for the longest-first order to even out
+    const int64_t min_big = p.cu_q != nullptr ? ATTN_FWD_PACKED_MIN_BIG
+                            : (causal || !ATTN_FWD_PP) ? ATTN_FWD_DENSE_MIN_BIG : ATTN_FWD_DENSE_MIN_BIG / 2;
     const bool big = p.B * p.Hq * ((p.Nq + NWB * 32 - 1) / (NWB * 32)) >= min_big;
     if (ATTN_FWD_PP && big && p.cu_q == nullptr) {
       if (p.d == 128) return causal ? launch_pp<128, true>(p, s) : launch_pp<128, false>(p, s);

@@ -142,13 +142,14 @@ def test_no_writes_outside_outputs():
 
 
 # ---------------------------------------------------------------- the 4-wave configuration at scale
-# The launcher runs the 8-wave kernel for at least 512 query tiles of 256
-# rows and the 4-wave kernel below that; the small shapes above take the
-# 4-wave kernel with few workgroups, these with many (up to 1022 tiles of
-# 128 rows), ragged and with Nq != Nk, on sampled rows, plus the 8-wave
-# kernel right at its threshold.
+# The launcher runs the 8-wave (two-group) kernel for at least 512 query
+# tiles of 256 rows when causal, 256 when not, and the 4-wave kernel below
+# that; the small shapes above take the 4-wave kernel with few workgroups,
+# these with many (up to 1022 tiles of 128 rows), ragged and with Nq != Nk,
+# on sampled rows, plus the 8-wave kernel right at its thresholds (the
+# non-causal cases of the 256..511-tile shapes).
 MIDDLE = [
-    # B, Hq, Hkv, Nq, Nk, d, expected configuration
+    # B, Hq, Hkv, Nq, Nk, d, configuration when causal
     (4, 16, 16, 2048, 2048, 128, "8-wave"),
     (1, 31, 31, 4096, 4096, 128, "4-wave"),  # 496 tiles of 256 rows, 992 workgroups
     (2, 32, 8, 1100, 1300, 64, "4-wave"),
@@ -158,15 +159,16 @@ MIDDLE = [
 ]
 
 
-def _config(B, Hq, Nq):
-    return "8-wave" if B * Hq * ((Nq + 255) // 256) >= 512 else "4-wave"
+def _config(B, Hq, Nq, causal):
+    return "8-wave" if B * Hq * ((Nq + 255) // 256) >= (512 if causal else 256) else "4-wave"
 
 
 @pytest.mark.parametrize("shape", MIDDLE)
 @pytest.mark.parametrize("causal", [True, False])
 def test_middle_grid_sampled_rows(oracle_mod, shape, causal):
     B, Hq, Hkv, Nq, Nk, d, cfg = shape
-    assert _config(B, Hq, Nq) == cfg
+    assert _config(B, Hq, Nq, True) == cfg
+    cfg = _config(B, Hq, Nq, causal)
     scale = 1.0 / math.sqrt(d)
     q, k, v = synth.attn_inputs(700 + Nq + d, B, Hq, Hkv, Nq, Nk, d, bf16=True)
     print(f"middle case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} ({cfg})", flush=True)
