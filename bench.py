@@ -766,7 +766,7 @@ def main():
         ach = f / t / 1e9
         # the launcher picks the 8-wave (256-row) configuration at this size:
         # 32 heads x 172 query tiles = 5504 workgroups of 512 threads
-        roofline = {"kernel": "fwd_pp_kernel<128, true> (5504 x 512)", "bound": "mfma", "achieved": round(ach, 2),
+        roofline = {"kernel": "fwd_pp_kernel<128, true, false, false> (5504 x 512)", "bound": "mfma", "achieved": round(ach, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                     "traffic": counted_traffic(FWD_COUNTERS)}
     sane = all(v.get("frac_mfma", 0) <= 1.0 and v.get("frac_hbm", 0) <= 1.0 for v in out_paths.values())
