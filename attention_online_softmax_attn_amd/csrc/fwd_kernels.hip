@@ -1093,14 +1093,17 @@ hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
   }
   if (p.bf16) {
     // 8 waves (256 query rows) per workgroup, which share each K/V tile (half
-    // the tile loads and barriers per query row of the 4-wave configuration).
-    // Dense problems take them once there are at least two such workgroups
-    // per CU over the launch: measured 3-8 % faster at N = 4096 and 8192 (32
-    // heads) and 2.6 % at 4 x 16 heads x 2048, 14 % slower with one per CU
-    // (N = 2048, 32 heads), where 4-wave workgroups, two per CU, fill the
-    // machine instead.  Packed batches, whose grid counts every sequence at
-    // the longest one's length, keep 4 waves up to 8 per CU (8 waves measured
-    // 9 % slower on 4 sequences of 600..2048 tokens, equal on 8).
+    // the tile loads and barriers per query row of the 4-wave configuration),
+    // run as the two-group kernel (fwd_pp_kernel; the one-group
+    // fwd_bf16_kernel<.., 8, ..> only with ATTN_FWD_PP=0).  Causal dense
+    // problems take them once there are at least two such workgroups per CU
+    // over the launch (the one-group kernel measured 3-8 % faster than 4
+    // waves at N = 4096 and 8192, 32 heads; with one per CU, N = 2048, 32
+    // heads, 14 % slower, and the two-group kernel 5-20 % slower), where
+    // 4-wave workgroups, two per CU, fill the machine instead.  Packed
+    // batches, whose grid counts every sequence at the longest one's length,
+    // keep 4 waves up to 8 per CU (8 waves measured 9 % slower on 4 sequences
+    // of 600..2048 tokens, equal on 8).
     constexpr int NWB = ATTN_FWD_BIG_NW, BNB = ATTN_FWD_BIG_BN;
     // a non-causal grid of equal workgroups fills the machine with one
     // two-group workgroup per CU (10 % faster at N = 2048, 32 heads, 256
