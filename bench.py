@@ -67,11 +67,28 @@ CSRC = os.path.join(ROOT, "attention_online_softmax_attn_amd", "csrc")
 FWD_COUNTERS = os.path.join(ROOT, "profiles", "fwd_bf16_prefill_n44032_hbm_counters.md")
 
 
+def source_digest(names, base=CSRC):
+    """SHA-256 of the named kernel sources with comments and white space
+    removed, so that a change of code, not of commentary, retires counters
+    taken on the earlier code; None if a file is missing."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for name in names:
+        try:
+            text = open(os.path.join(base, name), encoding="utf-8").read()
+        except OSError:
+            return None
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update((" ".join(text.split()) + "\n").encode())
+    return h.hexdigest()
+
+
 def counted_traffic(summary_path):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when the kernel sources have changed since the counters were taken."""
-    import hashlib
-
+    when the kernel code has changed since the counters were taken."""
     try:
         text = open(summary_path).read()
     except OSError:
@@ -84,13 +101,7 @@ def counted_traffic(summary_path):
                 fields[key[:-1]] = line[len(key):].strip()
     if len(fields) != 3:
         return None
-    h = hashlib.sha256()
-    for name in fields["source_files"].split():
-        try:
-            h.update(open(os.path.join(CSRC, name), "rb").read())
-        except OSError:
-            return None
-    if h.hexdigest() != fields["source_sha256"]:
+    if source_digest(fields["source_files"].split()) != fields["source_sha256"]:
         return None
     return int(fields["traffic_bytes_per_launch"])
 

@@ -41,19 +41,29 @@ def _summary(path, files, digest, traffic=123456789):
         f.write(f"    source_sha256: {digest}\n    traffic_bytes_per_launch: {traffic}\n")
 
 
+def test_source_digest_follows_code_not_comments(tmp_path):
+    src = "// header comment\n__global__ void k(int* p) {  /* block\ncomment */\n  p[0] = 1;  // store\n}\n"
+    (tmp_path / "a.hip").write_text(src)
+    d0 = bench.source_digest(["a.hip"], base=str(tmp_path))
+    (tmp_path / "a.hip").write_text("// another comment\n" + src.replace("  p[0]", "\n\n    p[0]"))
+    assert bench.source_digest(["a.hip"], base=str(tmp_path)) == d0
+    (tmp_path / "a.hip").write_text(src.replace("p[0] = 1", "p[0] = 2"))
+    assert bench.source_digest(["a.hip"], base=str(tmp_path)) != d0
+    # the digest of the bare code text, written out independently
+    code = "__global__ void k(int* p) { p[0] = 1; }"
+    assert d0 == hashlib.sha256((code + "\n").encode()).hexdigest()
+    assert bench.source_digest(["missing.hip"], base=str(tmp_path)) is None
+
+
 def test_counter_summary_is_used_only_for_the_sources_it_was_taken_on(tmp_path):
     files = ["fwd_kernels.hip", "device_common.hpp", "kernels.h"]
-    h = hashlib.sha256()
-    for name in files:
-        with open(os.path.join(bench.CSRC, name), "rb") as f:
-            h.update(f.read())
     good = tmp_path / "good.md"
-    _summary(good, files, h.hexdigest())
+    _summary(good, files, bench.source_digest(files))
     assert bench.counted_traffic(str(good)) == 123456789
     stale = tmp_path / "stale.md"
     _summary(stale, files, "0" * 64)
     assert bench.counted_traffic(str(stale)) is None
     missing = tmp_path / "missing.md"
-    _summary(missing, files + ["no_such_file.hip"], h.hexdigest())
+    _summary(missing, files + ["no_such_file.hip"], bench.source_digest(files))
     assert bench.counted_traffic(str(missing)) is None
     assert bench.counted_traffic(str(tmp_path / "absent.md")) is None
