@@ -214,8 +214,8 @@ __global__ __launch_bounds__(NWV * 64, 1) void decode_partial_kernel(DecArgs a) 
       const int r = p / CPR;
       const int cc = (p % CPR) ^ swz<D>(r);
       const uint32_t src = (uint32_t)(((row0 + r) * D + cc * 8) * 2);
-      buf_load_lds16(tk, src, (lds_void*)(kt + n * 1024));
-      buf_load_lds16(tv, src, (lds_void*)(vt + n * 1024));
+      buf_load_lds16_stream(tk, src, (lds_void*)(kt + n * 1024));
+      buf_load_lds16_stream(tv, src, (lds_void*)(vt + n * 1024));
     }
   };
 
@@ -415,8 +415,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_partial_fp8_kernel(DecA
       const int r = p / CPR;
       const int cc = (p % CPR) ^ (r % CPR);
       const uint32_t src = (uint32_t)((j0 + r) * D + cc * 16);
-      buf_load_lds16(rk, src, (lds_void*)(kt + n * 1024));
-      buf_load_lds16(rv, src, (lds_void*)(vt + n * 1024));
+      buf_load_lds16_stream(rk, src, (lds_void*)(kt + n * 1024));
+      buf_load_lds16_stream(rv, src, (lds_void*)(vt + n * 1024));
     }
   };
 
