@@ -649,11 +649,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgsF32 a) {
 #ifndef ATTN_FWD_PP_GROUPS
 #define ATTN_FWD_PP_GROUPS 1
 #endif
-// NT: O is stored non-temporally (launched for outputs larger than the 256 MB
-// MALL, which cannot stay in it: their write-back then does not land on the
-// kernel that runs next, e.g. 145 -> 141 us for a 48 x 4096 decode after the
-// 44k prefill, with the prefill itself unchanged)
-template <int D, bool CAUSAL, bool VARLEN = false, bool PAGED = false, bool NT = false>
+template <int D, bool CAUSAL, bool VARLEN = false, bool PAGED = false>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   constexpr int NW = 8, BM = NW * 32, BN = 64, KB = 2;
   constexpr int TILE_BYTES = BN * D * 2;
@@ -967,11 +963,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; e++) w[e] = to_bf16(acc[cb][4 * g4 + e] * inv);
-        bf16x4* dst = (bf16x4*)(orow + cb * 32 + 8 * g4 + 4 * h32);
-        if constexpr (NT)
-          __builtin_nontemporal_store(w, dst);
-        else
-          *dst = w;
+        *(bf16x4*)(orow + cb * 32 + 8 * g4 + 4 * h32) = w;
       }
     if (a.lse != nullptr && h32 == 0) a.lse[lse_row + qi] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
   }
@@ -1003,11 +995,7 @@ hipError_t launch_pp(const FwdProblem& p, hipStream_t s) {
   a.page = (int)p.page;
   a.max_pages = (int)p.max_pages;
   a.num_pages = (int)p.num_pages;
-  const int64_t o_rows = VARLEN ? p.tot_q : p.B * p.Nq;
-  if (!VARLEN && p.Hq * o_rows * D * 2 > ((int64_t)256 << 20))
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, false, false, true>), dim3(a.n_wgs), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, VARLEN, PAGED>), dim3(a.n_wgs), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, VARLEN, PAGED>), dim3(a.n_wgs), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
