@@ -38,14 +38,19 @@ struct SplitPlan {
 };
 
 // Choose the number of key chunks per (b, kv head) from a cost model of the
-// decode, with constants measured on MI355X at d = 128:
-//   - one workgroup streams its chunk at ~121 keys/us (bf16 cache; ~92 for
+// decode, with constants measured on MI355X at d = 128 (a sweep of every
+// split count at 1..48 streams x 1024..16384 keys, K/V streamed with the
+// non-temporal load policy):
+//   - one workgroup streams its chunk at ~90 keys/us (bf16 cache; ~92 for
 //     the FP8 kernel, which widens the codes in registers) after ~2 us of
 //     start-up, and the workgroups of a launch run in waves of one per CU
 //     (two for the FP8 kernel, whose tiles take half the LDS);
-//   - the whole decode reads at most ~5.6 TB/s;
-//   - each extra chunk costs ~0.2 us in the fold, and the two-launch path a
-//     further ~2.5 us for the merge launch.
+//   - the whole decode reads at most ~6.5 TB/s;
+//   - each extra chunk costs ~0.5 us in the fold, and the two-launch path a
+//     further ~4 us for the merge launch;
+//   - a decode call takes ~15 us whatever it streams (launch and
+//     synchronisation), so a cache the unsplit plan streams in less is not
+//     split (one stream of 1024 keys: 15.8 us unsplit, 19.1 us in 4 chunks).
 // Candidates are 1, 2, 4, ... chunks of at least one key tile, at most 64;
 // a larger count must beat the smaller by 5 % (the model's resolution).
 // Splitting pays only where too few workgroups would stream the cache: from
@@ -57,8 +62,9 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int request
   if (requested > 0) {
     s = requested;
   } else {
-    constexpr double kHbmBytesPerUs = 5.6e6, kWgStartUs = 2.0, kFoldUsPerSplit = 0.2, kMergeLaunchUs = 2.5;
-    const double keys_per_us = fp8 ? 92.0 : 121.0;
+    constexpr double kHbmBytesPerUs = 6.5e6, kWgStartUs = 2.0, kFoldUsPerSplit = 0.5, kMergeLaunchUs = 4.0;
+    constexpr double kCallFloorUs = 15.0;
+    const double keys_per_us = fp8 ? 92.0 : 90.0;
     const double slots = kNumCUs * (fp8 ? 2.0 : 1.0);
     const double units = (double)(B * Hkv);
     const double key_bytes = 2.0 * (double)d * (fp8 ? 1.0 : 2.0);  // K and V
@@ -74,6 +80,7 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int request
         best = t;
         s = (int)c;
       }
+      if (c == 1 && t < kCallFloorUs) break;
     }
   }
   if (s > tiles) s = (int)tiles;

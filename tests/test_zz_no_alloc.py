@@ -35,7 +35,8 @@ def _case(oracle_mod, seed, B, Hq, Hkv, Nk, d, splits):
 
 def test_noalloc_decode_two_calls_second_smaller(oracle_mod):
     _case(oracle_mod, 7100, 3, 32, 8, 3000, 128, 5)
-    _case(oracle_mod, 7101, 1, 16, 4, 700, 64, 0)
+    # the automatic plan splits one stream of 2000 keys (8 chunks)
+    _case(oracle_mod, 7101, 1, 16, 4, 2000, 64, 0)
 
 
 def test_noalloc_decode_rejects_plans_beyond_the_scratch():
