@@ -97,11 +97,12 @@ def strerror(status: int) -> str:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the argtypes declare c_void_p, which converts it
+    return None if t is None else t.data_ptr()
 
 
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -216,9 +217,10 @@ def attn_decode_splitkv(q, k, v, scale=None, num_splits: int = 0, workspace=None
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    need = decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().attn_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if want_lse else None, B, Hq, Hkv,
                                    Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _ptr(workspace), ws_bytes,
@@ -271,9 +273,10 @@ def attn_decode_splitkv_fused(q, k, v, scale=None, num_splits: int = 0, workspac
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    need = decode_fused_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = decode_fused_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
+        if need > 0:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().attn_decode_splitkv_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if want_lse else None, B, Hq,
                                          Hkv, Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _ptr(workspace),
@@ -306,9 +309,10 @@ def attn_decode_splitkv_fp8(q, k8, v8, k_scale, v_scale, scale=None, num_splits:
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    need = decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = decode_workspace_bytes(B, Hq, Hkv, Nk, d, num_splits)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().attn_decode_splitkv_fp8(_ptr(q), _ptr(k8), _ptr(v8), _ptr(k_scale), _ptr(v_scale), _ptr(o),
                                        _ptr(lse) if want_lse else None, B, Hq, Hkv, Nq, Nk, d, _scale(scale, d),
@@ -381,9 +385,10 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: i
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    need = decode_workspace_bytes(B, Hq, Hkv, int(max_seq_len), d, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = decode_workspace_bytes(B, Hq, Hkv, int(max_seq_len), d, num_splits)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(o),
                                  _ptr(lse) if want_lse else None, B, Hq, Hkv, d, num_pages, page,
@@ -418,9 +423,10 @@ def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale=None, workspace=
     dq = torch.empty(q.shape, **gd) if dq is None else dq
     dk = torch.empty(k.shape, **gd) if dk is None else dk
     dv = torch.empty(v.shape, **gd) if dv is None else dv
-    need = bwd_workspace_bytes(B, Hq, Nq, d)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = bwd_workspace_bytes(B, Hq, Nq, d)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = lib().attn_bwd if gdt == torch.float32 else lib().attn_bwd_bf16_grads
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B,
