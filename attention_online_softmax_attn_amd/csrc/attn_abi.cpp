@@ -27,8 +27,11 @@ attn_status check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (Nq > ATTN_MAX_SEQ || Nk > ATTN_MAX_SEQ) return ATTN_ERR_UNSUPPORTED;
-  // grid sizes must fit in 32-bit workgroup counts
+  // grid sizes must fit in 32-bit workgroup counts: no kernel takes fewer
+  // than 32 query rows per workgroup (the backward's key grid is bounded in
+  // attn_bwd)
   if (B * Hq > (int64_t)1 << 20) return ATTN_ERR_UNSUPPORTED;
+  if (B * Hq * ((Nq + 31) / 32) >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -403,6 +406,8 @@ static attn_status bwd_common(const void* q, const void* k, const void* v, const
   attn_status st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  // the dK/dV grid: 128 keys of one kv head per workgroup
+  if (B * Hkv * ((Nk + 31) / 32) >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
   if (Nq > 0 && (!q || !o || !dout || !lse || !dq)) return ATTN_ERR_INVALID;
   if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID;

@@ -26,7 +26,10 @@
  *   Types    dtype selects the element type of q, k, v, o and dout;
  *            accumulation is fp32; lse and all gradients are fp32
  *   Sizes    d must be 64 or 128; Hq % Hkv == 0; B, Nq, Nk >= 0; scale > 0
- *            and finite; Nq, Nk <= ATTN_MAX_SEQ
+ *            and finite; Nq, Nk <= ATTN_MAX_SEQ; B * Hq <= 2^20 and
+ *            B * Hq * ceil(Nq / 32) < 2^31, for attn_bwd also
+ *            B * Hkv * ceil(Nk / 32) < 2^31 (the launch grids' 32-bit
+ *            workgroup counts)
  *   Memory   every pointer is a device pointer owned by the caller; the
  *            library never allocates, frees or synchronises.  Inputs are
  *            read only; outputs are fully overwritten.  Workspaces are
@@ -57,7 +60,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, negative size, Hq % Hkv != 0, bad scale or dtype */
-  ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64,128}, size above ATTN_MAX_SEQ, dtype */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64,128}, size above the limits, dtype */
   ATTN_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than required */
   ATTN_ERR_HIP = 4,         /* a kernel launch failed */
   ATTN_ERR_SCRATCH = 5      /* the allocation-free decode needs more than ATTN_DECODE_SCRATCH_BYTES */

@@ -80,6 +80,8 @@ def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.1
         (dict(d=96), am.ATTN_ERR_UNSUPPORTED),
         (dict(d=256), am.ATTN_ERR_UNSUPPORTED),
         (dict(Nk=(1 << 22) + 1), am.ATTN_ERR_UNSUPPORTED),
+        (dict(B=1 << 11, Hq=1 << 10, Hkv=1 << 10), am.ATTN_ERR_UNSUPPORTED),          # B * Hq above 2^20
+        (dict(B=1 << 10, Hq=1 << 10, Hkv=1, Nq=1 << 22), am.ATTN_ERR_UNSUPPORTED),  # a query grid of 2^37 workgroups
     ],
 )
 def test_fwd_rejects(kw, code):
@@ -351,6 +353,10 @@ def test_bwd_rejects(fn):
     assert bwd(lse=NUL, fn=fn) == am.ATTN_ERR_INVALID
     assert bwd(dq=NUL, fn=fn) == am.ATTN_ERR_INVALID
     assert bwd(Hq=3, fn=fn) == am.ATTN_ERR_INVALID
+    # a key grid of 2^37 dK/dV workgroups (B * Hkv * Nk / 32), a query grid the common check accepts
+    big = getattr(am.lib(), fn)(P, P, P, P, P, P, P, P, P, 1 << 10, 1 << 10, 1 << 10, 1, 1 << 22, 128, 0.1, 1, P,
+                                1 << 40, am.ATTN_BF16, None)
+    assert big == am.ATTN_ERR_UNSUPPORTED
 
 
 def test_bwd_binding_refuses_other_gradient_dtypes():
