@@ -184,11 +184,12 @@ def test_bf16_grads_c5_tolerance_study(c5_case):
         print(f"  {name}: max|g| {gmax:.3f}  err fp32 {e32:.3e}  err bf16 {e16:.3e}", flush=True)
 
 
-def test_eight_wave_dq_ragged_gqa(oracle_mod):
+@pytest.mark.parametrize("causal,d", [(True, 128), (False, 128), (True, 64)])
+def test_eight_wave_dq_ragged_gqa(oracle_mod, causal, d):
     # 2 x 32 query heads over 8 kv heads at 2100 rows: 576 query tiles of 256
-    # rows, so dQ runs as eight-wave workgroups, with a ragged last tile and
-    # four query heads accumulated into each kv head's dK and dV; every head
-    # compared in full
-    B, Hq, Hkv, N, d = 2, 32, 8, 2100, 128
+    # rows, so dQ runs as eight-wave workgroups (the two-group kernel), with a
+    # ragged last tile and four query heads accumulated into each kv head's
+    # dK and dV; every head compared in full
+    B, Hq, Hkv, N = 2, 32, 8, 2100
     assert B * Hq * ((N + 255) // 256) >= 512
-    run_case(oracle_mod, 5700, B, Hq, Hkv, N, N, d, True)
+    run_case(oracle_mod, 5700 + d + int(causal), B, Hq, Hkv, N, N, d, causal)
