@@ -90,15 +90,35 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
+// 1: causal query tiles end at the last query row (tile t of T covers rows
+// Lq - BM (T - t) .. Lq - BM (T - 1 - t) - 1), so that the rows a ragged
+// length leaves over pad the first tile, which streams the fewest keys, not
+// the last, which streams them all.  Rows before 0 are padding: their Q row
+// is row 0's, their mask row 0's, and they are never stored.  Each stored
+// row sees the same key tiles in the same order either way.
+#ifndef ATTN_FWD_END_ALIGN
+#define ATTN_FWD_END_ALIGN 1
+#endif
+constexpr bool kEndAlign = ATTN_FWD_END_ALIGN != 0;
+
+// first query row of tile qt of a slice of Nq rows
+template <int BM, bool CAUSAL>
+__device__ __forceinline__ int qtile_row0(int qt, int Nq) {
+  if constexpr (CAUSAL && kEndAlign) return Nq - ((Nq + BM - 1) / BM - qt) * BM;
+  return qt * BM;
+}
+
 // Packed variable-length batch: the work item (sequence, query tile, query
 // head) of launch index `rank` in a longest-first order, computed by every
 // wave from the sequence offsets alone (no workspace, no host round trip).
 // An item's weight is the number of BN-key tiles its workgroup streams, the
-// kernel's own count: W(s, t) = ceil(min(Lk, min((t+1) BM, Lq) + Lk - Lq) / BN)
-// when causal (at least 0), ceil(Lk / BN) otherwise; it does not decrease with
-// t.  For a threshold w the items of sequence s with W >= w are its last
-// c_s(w) tiles, c_s(w) in closed form, so the weight of rank r is found by a
-// binary search on w over sum_s c_s(w), and ties go in (sequence, tile) order.
+// kernel's own count: when causal, with tile t of T ending at row e_t
+// (qtile_row0), W(s, t) = ceil(min(Lk, e_t + Lk - Lq) / BN) (at least 0), which
+// is ceil((Lk - BM (T - 1 - t)) / BN) for end-aligned tiles; ceil(Lk / BN)
+// otherwise.  It does not decrease with t, so for a threshold w the items of
+// sequence s with W >= w are its last c_s(w) tiles, c_s(w) in closed form, and
+// the weight of rank r is found by a binary search on w over sum_s c_s(w);
+// ties go in (sequence, tile) order.
 // Within an item the Hq heads take consecutive ranks, kv head first
 // (j -> kv head j % Hkv), so that the dispatcher, which sends launch index i
 // to XCD i % 8, keeps the query heads of one kv head together when Hkv is 8.
@@ -146,6 +166,7 @@ __device__ bool varlen_item(const FwdArgs& a, int rank, int& s_out, int& qt_out,
     const int x = (w - 1) * BN;  // W >= w  <=>  the streamed keys exceed x
     if (lk <= x) return 0;
     if (!CAUSAL) return n;
+    if constexpr (kEndAlign) return min(n, (lk - x + BM - 1) / BM);  // tile n - 1 - j streams Lk - BM j keys
     const int t = x - (lk - lq);  // need min((qt + 1) BM, Lq) > t
     if (lq <= t) return 0;
     return n - (t < 0 ? 0 : t / BM);
@@ -242,9 +263,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     kvh = wi.pair % a.Hkv;
   }
 
-  const int i0 = qt * BM;
-  const int qw0 = i0 + wave * 32;
-
   // this (batch or sequence, head) slice: its sizes and element offsets
   int Nq = a.Nq, Nk = a.Nk;
   size_t q_head, kv_head, lse_row;
@@ -268,6 +286,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)Nk * D;
     lse_row = ((size_t)b * a.Hq + hq) * (size_t)Nq;
   }
+  const int i0 = qtile_row0<BM, CAUSAL>(qt, Nq);
+  const int qw0 = i0 + wave * 32;
+  // rows before 0 pad the first tile: they take row 0's Q and mask
+  constexpr bool LEAD_PAD = CAUSAL && kEndAlign;
+  auto lo_row = [](int r) { return LEAD_PAD ? max(r, 0) : r; };
   if (i0 >= Nq) return;  // the whole workgroup: a tile past this sequence's queries
   const int off = Nk - Nq;  // causal: key j visible to query i iff j <= i + off
 
@@ -326,7 +349,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; s++) {
-    const uint32_t src = (uint32_t)(((qw0 + l32) * D + 16 * s + 8 * h32) * 2);
+    const uint32_t src = (uint32_t)((lo_row(qw0 + l32) * D + 16 * s + 8 * h32) * 2);
     qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, src));
   }
 
@@ -360,7 +383,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     const char* vt = vcur + SUB * KS * (D * 2);
     const int j0 = t * BN + SUB * KS;
     // wave-level classification of the sub-tile
-    if (j0 >= Nk) return;
+    if (j0 >= Nk || qw0 >= Nq || (LEAD_PAD && qw0 + 31 < 0)) return;  // past the keys, or a wave of padding rows
     bool need_mask = (j0 + KS > Nk);
     if (CAUSAL) {
       if (j0 > qw0 + 31 + off) return;               // nothing visible to this wave
@@ -382,7 +405,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       // key j = j0 + 4h + c (c = kb*32 + 8(r/4) + r%4, a constant per
       // element) is visible iff j < Nk and, causal, j <= qi + off: one lane
       // bound lim on c, so each element costs one compare with a constant
-      const int lim = (CAUSAL ? min(Nk, qi + off + 1) : Nk) - j0 - 4 * h32;
+      const int lim = (CAUSAL ? min(Nk, lo_row(qi) + off + 1) : Nk) - j0 - 4 * h32;
 #pragma unroll
       for (int kb = 0; kb < KB; kb++)
 #pragma unroll
@@ -486,7 +509,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qi < Nq) {
+  if ((!LEAD_PAD || qi >= 0) && qi < Nq) {
     __bf16* orow = a.o + q_head + (size_t)qi * D;
 #pragma unroll
     for (int cb = 0; cb < D / 32; cb++)
@@ -679,8 +702,6 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     b = wi.pair / a.Hkv;
     kvh = wi.pair % a.Hkv;
   }
-  const int i0 = qt * BM;
-  const int qw0 = i0 + wave * 32;
   int Nq = a.Nq, Nk = a.Nk;
   size_t q_head, kv_head, lse_row;
   if constexpr (VARLEN) {
@@ -698,12 +719,17 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       Nk = k1 - k0;
       kv_head = ((size_t)kvh * a.tot_k + k0) * D;
     }
-    if (i0 >= Nq) return;  // the whole workgroup: a tile past this sequence's queries
   } else {
     q_head = ((size_t)b * a.Hq + hq) * (size_t)Nq * D;
     kv_head = ((size_t)b * a.Hkv + kvh) * (size_t)Nk * D;
     lse_row = ((size_t)b * a.Hq + hq) * (size_t)Nq;
   }
+  const int i0 = qtile_row0<BM, CAUSAL>(qt, Nq);
+  const int qw0 = i0 + wave * 32;
+  // rows before 0 pad the first tile: they take row 0's Q and mask
+  constexpr bool LEAD_PAD = CAUSAL && kEndAlign;
+  auto lo_row = [](int r) { return LEAD_PAD ? max(r, 0) : r; };
+  if (VARLEN && i0 >= Nq) return;  // the whole workgroup: a tile past this sequence's queries
   const int off = Nk - Nq;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + q_head, (uint32_t)Nq * D * 2);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head, (uint32_t)Nk * D * 2);
@@ -766,7 +792,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; s++)
-    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(((qw0 + l32) * D + 16 * s + 8 * h32) * 2)));
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)((lo_row(qw0 + l32) * D + 16 * s + 8 * h32) * 2)));
   // Q, K(0) and V(0) complete here, so that no later counted wait has to
   // cover the Q registers
   wait_vmem();
@@ -790,9 +816,17 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   f32x16 st[KB];      // S^T of the tile between its MFMA and VALU phases
   bf16x8 pb[KB][2];   // P of the tile between its VALU phase and the next MFMA phase
 
-  auto visible = [&](int t) __attribute__((always_inline)) {
-    return t >= 0 && t < n && (!CAUSAL || t * BN <= qw0 + 31 + off);
-  };
+  // the tiles this wave computes, 0 .. n_vis - 1: up to its last row's
+  // diagonal when causal, and none for a wave whose 32 rows all lie past the
+  // last query (the ragged tile's padding), which takes part in the loads and
+  // barriers only
+  int n_vis = n;
+  if (CAUSAL) {
+    const int x = qw0 + 31 + off;  // tile t is visible iff t * BN <= x
+    n_vis = x < 0 ? 0 : min(n, x / BN + 1);
+  }
+  if (qw0 >= Nq || (LEAD_PAD && qw0 + 31 < 0)) n_vis = 0;
+  auto visible = [&](int t) __attribute__((always_inline)) { return t >= 0 && t < n_vis; };
   // MFMA phase of tile t: P V of tile t - 1 (V in vp), S^T of tile t (K in kc)
   auto mfma_phase = [&](int t, const char* __restrict__ kc, const char* __restrict__ vp)
                         __attribute__((always_inline)) {
@@ -850,7 +884,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     bool need_mask = (j0 + BN > Nk);
     if (CAUSAL && j0 + BN - 1 > qw0 + off) need_mask = true;
     if (need_mask) {
-      const int lim = (CAUSAL ? min(Nk, qi + off + 1) : Nk) - j0 - 4 * h32;
+      const int lim = (CAUSAL ? min(Nk, lo_row(qi) + off + 1) : Nk) - j0 - 4 * h32;
 #pragma unroll
       for (int kb = 0; kb < KB; kb++)
 #pragma unroll
@@ -954,7 +988,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qi < Nq) {
+  if ((!LEAD_PAD || qi >= 0) && qi < Nq) {
     __bf16* orow = a.o + q_head + (size_t)qi * D;
 #pragma unroll
     for (int cb = 0; cb < D / 32; cb++)
