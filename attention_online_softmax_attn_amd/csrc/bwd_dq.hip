@@ -140,6 +140,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     constexpr int kb = decltype(kbc)::value;
     const int j0 = t * BN + kb * 32;
     if (CAUSAL && j0 > qw0 + 31 + off) return;  // no key of the block visible to this wave
+    if (qw0 >= a.Nq) return;                     // a wave of padding rows
     const bool need_mask = (j0 + 32 > a.Nk) || (qw0 + 32 > a.Nq) || (CAUSAL && j0 + 31 > qw0 + off);
     const char* kt = kcur + kb * 32 * (D * 2);
     const char* vt = vcur + kb * 32 * (D * 2);
@@ -346,10 +347,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_pp_kernel(BwdArgs a) {
   f32x16 st[2], dpt[2];  // S^T, dP^T of a tile's two halves between its MFMA and VALU phases
   bf16x8 sb[2][2];       // dS^T of the two halves between the VALU phase and the next MFMA phase
 
-  // half kb of tile t has keys this wave's rows see
-  auto visible = [&](int t, int kb) __attribute__((always_inline)) {
-    return t >= 0 && t < n && (!CAUSAL || t * BN + kb * 32 <= qw0 + 31 + off);
-  };
+  // half kb of tile t has keys this wave's rows see: halves 0 .. n_vis - 1
+  // (up to the last row's diagonal when causal; none for a wave whose rows
+  // all lie past the last query)
+  int n_vis = 2 * n;
+  if (CAUSAL) {
+    const int x = qw0 + 31 + off;  // half h is visible iff 32 h <= x
+    n_vis = x < 0 ? 0 : min(2 * n, x / 32 + 1);
+  }
+  if (qw0 >= a.Nq) n_vis = 0;
+  auto visible = [&](int t, int kb) __attribute__((always_inline)) { return t >= 0 && 2 * t + kb < n_vis; };
   // MFMA phase of tile t: dQ of tile t - 1 (K in kp), S^T and dP^T of tile t
   // (K, V in kc, vc)
   auto mfma_phase = [&](int t, const char* __restrict__ kp, const char* __restrict__ kc,
