@@ -92,13 +92,25 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int request
   return {eff, (int)chunk};
 }
 
-// The paged decode's plan.  Streams of unequal length leave whole-length
-// chunks unbalanced (the longest stream's run decides the end): from 2048
-// keys on the automatic plan takes at least two chunks, which measured 1-15 %
-// faster at 48 streams of 512..4096, 4096 and 64..8192 keys.
+// The paged decode's plan.  Its kernel starts the longest (stream, chunk)
+// items first, so unequal lengths alone need no split; the cost model, which
+// takes every stream at the longest length, then gets two floors measured at
+// 8..48 streams of 64..16384 keys: chunks of at most 4096 keys (48 streams of
+// 8192 keys: 260 us in two chunks against 278 in one; of 1024..12288: 205 in
+// three against 222), but no split into chunks of 2048 keys or fewer where
+// the streams fill the CUs (48 of 512..4096: 92.7 us unsplit, 101.9 in two);
+// and with fewer (stream, kv head) pairs than CUs, enough chunks of at least
+// 1024 keys to give each CU one (16 streams of 512..4096: 42.7 us in two
+// chunks against 51.9 in one).
 SplitPlan paged_plan(int64_t B, int64_t Hkv, int64_t max_seq_len, int64_t d, int requested) {
-  if (requested == 0 && max_seq_len >= 2048)
-    requested = std::max(2, plan_splits(B, Hkv, max_seq_len, d, 0, false, false).splits);
+  if (requested == 0) {
+    int64_t s = plan_splits(B, Hkv, max_seq_len, d, 0, false, false).splits;
+    s = std::max<int64_t>(s, max_seq_len / 4096);
+    const int64_t pairs = B * Hkv;
+    if (pairs > 0 && pairs < kNumCUs)
+      s = std::max<int64_t>(s, std::min<int64_t>((kNumCUs + pairs - 1) / pairs, max_seq_len / 1024));
+    requested = (int)std::min<int64_t>(s, 64);
+  }
   return plan_splits(B, Hkv, max_seq_len, d, requested, false, false);
 }
 

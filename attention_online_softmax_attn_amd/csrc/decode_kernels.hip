@@ -134,6 +134,29 @@ __device__ void merge_if_last(const DecArgs& a, int b, int kvh, int pair) {
   if (threadIdx.x == 0) atomicExch(a.counters + pair, 0u);
 }
 
+// Paged caches: the streams differ in length, so the launch order follows each
+// (stream, chunk) item's own weight, longest first (lpt_place), instead of the
+// dense grid's (stream, kv head, chunk) order, where a long stream's chunks
+// could start last and run alone at the end.  Chunk s of a stream of L keys
+// holds clamp(L - s chunk, 0, chunk) keys and weighs its 32-key tiles, so the
+// chunks of weight >= w are a stream's first ones; the Hkv heads of an item
+// take consecutive launch indices.  Empty chunks come last and only store an
+// empty state for the merge.
+__device__ __forceinline__ void paged_decode_item(const DecArgs& a, int rank, int& b, int& kvh, int& split) {
+  const int lim = min(a.Nk, a.max_pages * a.page);
+  auto size = [&](int s) -> int2 { return make_int2(min(max(a.seq_lens[s], 0), lim), 0); };
+  auto count = [&](int2 sz, int w) -> int {
+    if (w <= 0) return a.S;
+    const int y = (w - 1) * kDecodeTile;  // weight >= w  <=>  more than y keys
+    if (y >= a.chunk || sz.x <= y) return 0;
+    return min(a.S, (sz.x - y + a.chunk - 1) / a.chunk);
+  };
+  int2 sz;
+  int c_lo, c_lo1, k;
+  lpt_place<4>(a.B, a.Hkv, rank, a.chunk / kDecodeTile + 2, size, count, b, sz, c_lo, c_lo1, k, kvh);
+  split = c_lo1 + k;
+}
+
 template <int D, bool PAGED, int NWV>
 __global__ __launch_bounds__(NWV * 64, 1) void decode_partial_kernel(DecArgs a) {
   constexpr int BN = kDecodeTile;
@@ -157,9 +180,16 @@ __global__ __launch_bounds__(NWV * 64, 1) void decode_partial_kernel(DecArgs a) 
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
-  const int work = xcd_remap(blockIdx.x, a.n_wgs);
-  const int split = work % a.S;
-  const int pair = work / a.S;
+  int split, pair;
+  if constexpr (PAGED) {
+    int bi, hi;
+    paged_decode_item(a, (int)blockIdx.x, bi, hi, split);
+    pair = bi * a.Hkv + hi;
+  } else {
+    const int work = xcd_remap(blockIdx.x, a.n_wgs);
+    split = work % a.S;
+    pair = work / a.S;
+  }
   const int b = pair / a.Hkv;
   const int kvh = pair % a.Hkv;
 
@@ -601,8 +631,9 @@ hipError_t launch(const DecodeProblem& p, hipStream_t s) {
   // kv heads: 2-10 % faster at 512..4096 keys; 2-wave workgroups on a grid of
   // at most 256 leave half the CU slots empty and measured 2-16 % slower).
   // Paged caches keep 4 waves: their streams differ in length, the longest
-  // stream's chunks decide the end, and a 2-wave workgroup streams a chunk at
-  // half the rate (14 % slower at 48 streams of 512..4096 keys).
+  // chunks (launched first) decide the end, and a 2-wave workgroup streams a
+  // chunk at half the rate (48 streams of 512..4096 keys: 103.9 against 92.7
+  // us in one chunk, 96.8 in two).
   const bool two = a.n_wgs > 256;
   if (p.block_table != nullptr) {
     hipLaunchKernelGGL((decode_partial_kernel<D, true, 4>), dim3(a.n_wgs), dim3(256), 0, s, a);

@@ -177,6 +177,96 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
   return start + t;
 }
 
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Longest-first placement of work items of unequal size, computed by every
+// wave from per-sequence sizes on the device (no workspace, no host round
+// trip).  Sequence s has size(s) (one or two numbers) and count(size, w)
+// items of weight at least w: a count that does not increase with w, is the
+// sequence's whole item count at w = 0 and 0 at w = w_end.  Ranks go to the
+// items heaviest first, ties in sequence order, each item taking n_heads
+// consecutive ranks; the weight of rank r is found by a binary search on w
+// over the summed counts.  Rank `rank` is placed on sequence s_out (whose
+// size comes back in size_out) as the k_out-th, in the sequence's own order,
+// of its items of weight exactly w, where c_lo = count(size, w) and c_lo1 =
+// count(size, w + 1), and on head slot j_out.  The sizes of the first
+// kCached * 64 sequences stay in registers.  Returns false for a rank past
+// the last item.
+template <int kCached, class Size, class Count>
+__device__ bool lpt_place(int n_seqs, int n_heads, int rank, int w_end, Size size, Count count, int& s_out,
+                          int2& size_out, int& c_lo, int& c_lo1, int& k_out, int& j_out) {
+  const int lane = threadIdx.x & 63;
+  int2 sz_c[kCached];
+#pragma unroll
+  for (int c = 0; c < kCached; c++) {
+    sz_c[c] = make_int2(0, 0);
+    const int s = c * 64 + lane;
+    if (s < n_seqs) sz_c[c] = size(s);
+  }
+  auto get = [&](int c) -> int2 {
+    if (c < kCached) {
+      // constant-indexed copies, so that the array stays in registers
+      int2 v = sz_c[0];
+#pragma unroll
+      for (int i = 1; i < kCached; i++)
+        if (c == i) v = sz_c[i];
+      return v;
+    }
+    return c * 64 + lane < n_seqs ? size(c * 64 + lane) : make_int2(0, 0);
+  };
+  const int chunks = (n_seqs + 63) / 64;
+  auto total = [&](int w) -> int {
+    int c_sum = 0;
+    for (int c = 0; c < chunks; c++) c_sum += count(get(c), w);
+    return wave_sum(c_sum);
+  };
+  if (rank >= total(0) * n_heads) return false;
+  // the largest w whose items (times heads) outnumber rank
+  int lo = 0, hi = w_end;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (total(mid) * n_heads > rank) lo = mid;
+    else hi = mid;
+  }
+  const int r2 = rank - total(lo + 1) * n_heads;  // index among the items of weight exactly lo
+  const int u = r2 / n_heads;
+  j_out = r2 % n_heads;
+  int before = 0;
+  for (int c = 0; c < chunks; c++) {
+    const int2 sz = get(c);
+    const int cw = count(sz, lo), cw1 = count(sz, lo + 1);
+    const int e = cw - cw1;
+    const int incl = wave_incl_scan(e, lane);
+    const int excl = incl - e;
+    const bool hit = e > 0 && before + excl <= u && u < before + incl;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+    if (m != 0) {
+      const int src = (int)__builtin_ctzll(m);
+      s_out = c * 64 + src;
+      size_out = make_int2(__builtin_amdgcn_readlane(sz.x, src), __builtin_amdgcn_readlane(sz.y, src));
+      c_lo = __builtin_amdgcn_readlane(cw, src);
+      c_lo1 = __builtin_amdgcn_readlane(cw1, src);
+      k_out = u - before - __builtin_amdgcn_readlane(excl, src);
+      return true;
+    }
+    before += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return false;  // not reached: the counts above place every rank
+}
+
 // Launch index -> (pair, sub) for a grid of n_pairs * per_pair workgroups
 // whose sub 0 is the heaviest item of a pair and later subs are lighter.  The
 // dispatcher sends workgroup pid to XCD pid % 8 and starts the workgroups of

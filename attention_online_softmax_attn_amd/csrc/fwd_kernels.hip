@@ -75,21 +75,6 @@ __device__ __forceinline__ int snake_pid(int pid, int n, int on) {
   return x + 8 * (t < half ? t : T - 1 - (t - half));
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return __builtin_amdgcn_readfirstlane(x);
-}
-
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
 // 1: causal query tiles end at the last query row (tile t of T covers rows
 // Lq - BM (T - t) .. Lq - BM (T - 1 - t) - 1), so that the rows a ragged
 // length leaves over pad the first tile, which streams the fewest keys, not
@@ -125,42 +110,19 @@ __device__ __forceinline__ int qtile_row0(int qt, int Nq) {
 // Returns false for a rank past the last item.
 template <int BM, int BN, bool CAUSAL, bool PAGED>
 __device__ bool varlen_item(const FwdArgs& a, int rank, int& s_out, int& qt_out, int& h_out) {
-  const int lane = threadIdx.x & 63;
-  const int n_seqs = a.B;
-  constexpr int kCached = 4;  // sequences 0 .. 255 stay in registers
-  // the kernel's own clamped per-sequence sizes
-  auto sizes = [&](int s, int& lq, int& lk) {
+  // the kernel's own clamped per-sequence sizes (Lq, Lk)
+  auto size = [&](int s) -> int2 {
     const int q1 = min(a.cu_q[s + 1], a.tot_q), q0 = max(0, min(a.cu_q[s], q1));
-    lq = q1 - q0;
     if constexpr (PAGED) {
-      lk = min(max(a.seq_lens_k[s], 0), min(a.Nk, a.max_pages * a.page));
+      return make_int2(q1 - q0, min(max(a.seq_lens_k[s], 0), min(a.Nk, a.max_pages * a.page)));
     } else {
       const int k1 = min(a.cu_k[s + 1], a.tot_k), k0 = max(0, min(a.cu_k[s], k1));
-      lk = k1 - k0;
-    }
-  };
-  int lq_c[kCached], lk_c[kCached];
-#pragma unroll
-  for (int c = 0; c < kCached; c++) {
-    lq_c[c] = 0;
-    lk_c[c] = 0;
-    const int s = c * 64 + lane;
-    if (s < n_seqs) sizes(s, lq_c[c], lk_c[c]);
-  }
-  auto get = [&](int c, int& lq, int& lk) {
-    if (c < kCached) {
-      // constant-indexed copies, so that the arrays stay in registers
-      lq = lq_c[0], lk = lk_c[0];
-#pragma unroll
-      for (int i = 1; i < kCached; i++)
-        if (c == i) lq = lq_c[i], lk = lk_c[i];
-    } else {
-      lq = lk = 0;
-      if (c * 64 + lane < n_seqs) sizes(c * 64 + lane, lq, lk);
+      return make_int2(q1 - q0, k1 - k0);
     }
   };
   // items of one sequence whose weight is at least w
-  auto count_s = [&](int lq, int lk, int w) -> int {
+  auto count = [&](int2 sz, int w) -> int {
+    const int lq = sz.x, lk = sz.y;
     const int n = (lq + BM - 1) / BM;
     if (w <= 0) return n;
     const int x = (w - 1) * BN;  // W >= w  <=>  the streamed keys exceed x
@@ -171,49 +133,15 @@ __device__ bool varlen_item(const FwdArgs& a, int rank, int& s_out, int& qt_out,
     if (lq <= t) return 0;
     return n - (t < 0 ? 0 : t / BM);
   };
-  const int chunks = (n_seqs + 63) / 64;
-  auto count = [&](int w) -> int {
-    int c_sum = 0;
-    for (int c = 0; c < chunks; c++) {
-      int lq, lk;
-      get(c, lq, lk);
-      c_sum += count_s(lq, lk, w);
-    }
-    return wave_sum(c_sum);
-  };
-  const int total = count(0);
-  if (rank >= total * a.Hq) return false;
-  // the largest w whose items (times heads) outnumber rank
-  int lo = 0, hi = a.Nk / BN + 2;  // count(hi) == 0
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (count(mid) * a.Hq > rank) lo = mid;
-    else hi = mid;
-  }
-  const int r2 = rank - count(lo + 1) * a.Hq;  // index among the items of weight exactly lo
-  const int u = r2 / a.Hq, j = r2 % a.Hq;
-  int before = 0;
-  for (int c = 0; c < chunks; c++) {
-    int lq, lk;
-    get(c, lq, lk);
-    const int cw = count_s(lq, lk, lo);
-    const int e = cw - count_s(lq, lk, lo + 1);
-    const int incl = wave_incl_scan(e, lane);
-    const int excl = incl - e;
-    const bool hit = e > 0 && before + excl <= u && u < before + incl;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
-    if (m != 0) {
-      const int src = (int)__builtin_ctzll(m);
-      const int n = (lq + BM - 1) / BM;
-      s_out = c * 64 + src;
-      qt_out = __builtin_amdgcn_readlane(n - cw + (u - before - excl), src);
-      const int g = a.Hq / a.Hkv;
-      h_out = (j % a.Hkv) * g + j / a.Hkv;
-      return true;
-    }
-    before += __builtin_amdgcn_readlane(incl, 63);
-  }
-  return false;  // not reached: the counts above place every rank
+  int2 sz;
+  int c_lo, c_lo1, k, j;
+  if (!lpt_place<4>(a.B, a.Hq, rank, a.Nk / BN + 2, size, count, s_out, sz, c_lo, c_lo1, k, j)) return false;
+  // the items of weight >= w are a sequence's last count(w) tiles
+  qt_out = (sz.x + BM - 1) / BM - c_lo + k;
+  // within an item the Hq heads take consecutive ranks, kv head first
+  const int g = a.Hq / a.Hkv;
+  h_out = (j % a.Hkv) * g + j / a.Hkv;
+  return true;
 }
 
 template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>

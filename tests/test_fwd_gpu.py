@@ -174,7 +174,12 @@ def test_middle_grid_sampled_rows(oracle_mod, shape, causal):
     print(f"middle case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} ({cfg})", flush=True)
     o, lse = attn_fwd(dev(q, True), dev(k, True), dev(v, True), causal=causal, scale=scale)
     torch.cuda.synchronize()
-    forced = (0, 1, 63, 64, 127, 128, 129, Nq // 2, Nq - 65, Nq - 2, Nq - 1)
+    # causal query tiles end at the last row, so their boundaries sit at
+    # Nq mod BM + k BM (the first tile holds the padding); both sides of the
+    # first two boundaries are forced
+    bm = 256 if cfg == "8-wave" else 128
+    r0 = Nq % bm
+    forced = (0, 1, 63, 64, 127, 128, 129, Nq // 2, Nq - 65, Nq - 2, Nq - 1, r0 - 1, r0, r0 + bm - 1, r0 + bm)
     rows = synth.sample_rows(40007 + Nq, 192, B, Hq, Nq, forced_i=forced)
     eo, el = oracle_mod.fwd_rows(q, k, v, rows, scale, causal)
     idx = (rows[:, 0], rows[:, 1], rows[:, 2])
@@ -205,7 +210,8 @@ def test_large_grid_sampled_rows(oracle_mod, shape, causal):
     print(f"large case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal}", flush=True)
     o, lse = attn_fwd(dev(q, True), dev(k, True), dev(v, True), causal=causal, scale=scale)
     torch.cuda.synchronize()
-    forced = (0, 1, 63, 64, 255, 256, 257, Nq // 2, Nq - 65, Nq - 2, Nq - 1)
+    r0 = Nq % 256  # first boundary of the end-aligned causal tiles
+    forced = (0, 1, 63, 64, 255, 256, 257, Nq // 2, Nq - 65, Nq - 2, Nq - 1, r0 - 1, r0, r0 + 255, r0 + 256)
     rows = synth.sample_rows(40005 + Nq, 192, B, Hq, Nq, forced_i=forced)
     eo, el = oracle_mod.fwd_rows(q, k, v, rows, scale, causal)
     idx = (rows[:, 0], rows[:, 1], rows[:, 2])
