@@ -249,9 +249,12 @@ attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* 
  *            every seq_lens entry; it sizes the split plan and the
  *            workspace, attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len,
  *            d, num_splits), which also covers this entry point's
- *            automatic plan: attn_decode_splitkv's, but at least 2 chunks
- *            from max_seq_len >= 2048 on (unequal lengths unbalance whole-
- *            length chunks).  A stream with no keys gets O = 0, LSE = -inf.
+ *            automatic plan: attn_decode_splitkv's, raised to chunks of at
+ *            most 4096 keys and, with fewer (stream, kv head) pairs than
+ *            the 256 CUs, to enough chunks of at least 1024 keys to give
+ *            each CU one.  The (stream, chunk) items start longest first
+ *            (ordered on the device from seq_lens), so unequal lengths need
+ *            no further split.  A stream with no keys gets O = 0, LSE = -inf.
  *   Other    q, o bf16 [B, Hq, 1, d]; lse fp32 [B, Hq] (may be NULL);
  *            max_pages * page_size <= ATTN_MAX_SEQ; every other rule as
  *            attn_decode_splitkv.
