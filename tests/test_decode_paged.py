@@ -67,6 +67,9 @@ CASES = [
     ([300, 0, 129, 64], 4, 4, 64, 64),
     ([256, 255, 1000], 16, 2, 256, 128),
     ([5000, 17], 2, 1, 128, 64),
+    # 300 streams: past the 256 whose lengths the longest-first placement
+    # keeps in registers, the rest read again from seq_lens
+    ([int(x) for x in np.random.default_rng(302).integers(0, 200, size=300)], 8, 2, 32, 64),
 ]
 
 

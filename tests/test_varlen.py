@@ -75,6 +75,14 @@ SMALL = [
     ([300, 1, 129], [700, 513, 129], 8, 2, 64),
 ]
 
+# 300 short sequences: past the 256 whose sizes the item placement keeps in
+# registers, so the rest are read again from the offsets; 300 x 8 heads reach
+# the two-group kernel
+_r300 = np.random.default_rng(300)
+LQ300 = [int(x) for x in _r300.integers(0, 41, size=300)]
+LK300 = [lq + int(h) for lq, h in zip(LQ300, _r300.integers(0, 61, size=300))]
+SMALL.append((LQ300, LK300, 8, 2, 64))
+
 
 # Packed batches of at least 2048 tiles of 256 rows (every sequence counted at
 # the longest one's length) take the two-group 8-wave kernel: here one

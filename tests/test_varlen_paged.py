@@ -64,6 +64,12 @@ CASES = [
 ]
 
 
+# 300 short sequences (past the 256 whose sizes the item placement keeps in
+# registers; 300 x 4 heads take the 4-wave kernel)
+_r300 = np.random.default_rng(301)
+_lq300 = [int(x) for x in _r300.integers(0, 41, size=300)]
+CASES.append((_lq300, [lq + int(h) for lq, h in zip(_lq300, _r300.integers(0, 100, size=300))], 4, 2, 64, 64))
+
 def _dev_cache(kc, vc, used):
     import torch
 
