@@ -31,13 +31,19 @@ FLAGS = [
 ]
 
 
-# Per-source scheduling: the dK/dV kernel runs one wave per SIMD, so its LDS
-# operand reads must be issued well ahead of the MFMAs that use them and the
-# exponentials interleaved with independent MFMAs; the ILP-maximising machine
-# scheduler does that, the default (occupancy-driven) one sinks every read next
-# to its use.  The dQ kernel (bwd_dq.hip) measured faster with the default.
+# Per-source machine schedulers for the backward's kernels, chosen by timing
+# every strategy of the compiler on both (same bits with each): the dK/dV
+# kernel runs one wave per SIMD, so its LDS operand reads must be issued well
+# ahead of the MFMAs that use them, which the default (occupancy-driven)
+# scheduler does not do (it sinks every read next to its use); the dQ
+# kernel's two wave groups gain from the ILP-driven ones as well.  At B=4
+# H=16 N=2048 causal the backward took 297.5 us with dK/dV under max-ilp and
+# dQ under the default, 289.7 with both under max-ilp, 287.0 with these (five
+# interleaved rounds, one job); at grouped-query N=4096 and N=8192 and at
+# d = 64 they are within 1 % of the best pair.
 SOURCE_FLAGS = {
-    "bwd_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "bwd_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
+    "bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 
