@@ -101,7 +101,16 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+# torch's current stream of the current device as a raw handle: the
+# C-level getter returns the same handle as current_stream().cuda_stream
+# without building a Stream object (2.8 of the 9.6 us a tiny forward call
+# spent on the host); the public form serves where the getter is absent
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream():
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
     return torch.cuda.current_stream().cuda_stream
 
 

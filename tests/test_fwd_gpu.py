@@ -132,6 +132,25 @@ def test_repeatable_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_runs_on_the_callers_stream():
+    # the binding passes the current stream's handle: inside a side stream's
+    # context the call is ordered on that stream and gives the same bits
+    q, k, v = synth.attn_inputs(404, 2, 8, 2, 300, 300, 128, bf16=True)
+    qd, kd, vd = dev(q, True), dev(k, True), dev(v, True)
+    o1, l1 = attn_fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    o2 = torch.full_like(o1, float("nan"))
+    l2 = torch.full_like(l1, float("nan"))
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        import attention_online_softmax_attn_amd as am
+        assert am._stream() == side.cuda_stream
+        attn_fwd(qd, kd, vd, causal=True, out=o2, lse=l2)
+    side.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_no_writes_outside_outputs():
     q, k, v = synth.attn_inputs(403, 1, 4, 2, 130, 130, 128, bf16=True)
     o, ofull = guarded_empty(q.shape, torch.bfloat16)
