@@ -81,6 +81,12 @@ __device__ __forceinline__ int snake_pid(int pid, int n, int on) {
 // the last, which streams them all.  Rows before 0 are padding: their Q row
 // is row 0's, their mask row 0's, and they are never stored.  Each stored
 // row sees the same key tiles in the same order either way.
+// 1: the two-group kernel stores O through LDS, four whole rows per store
+// instruction, instead of 16-byte pieces of 32 rows (0); 2: the same with
+// non-temporal stores
+#ifndef ATTN_FWD_O_STAGE
+#define ATTN_FWD_O_STAGE 1
+#endif
 #ifndef ATTN_FWD_END_ALIGN
 #define ATTN_FWD_END_ALIGN 1
 #endif
@@ -916,6 +922,43 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+#if ATTN_FWD_O_STAGE
+  // O through LDS: each wave writes its 32 rows into the (now free) K/V
+  // buffers, two waves per buffer, and stores them back four whole rows per
+  // instruction instead of 16-byte pieces of 32 rows
+  static_assert(2 * 32 * D * 2 <= TILE_BYTES, "two waves' rows per buffer");
+  __syncthreads();  // every wave is done with the K/V buffers
+  char* const obuf = ((wave >> 1) == 0 ? k_st0 : (wave >> 1) == 1 ? k_st1 : (wave >> 1) == 2 ? k_st2 : v_st0) +
+                     (wave & 1) * (32 * D * 2);
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; g4++) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; e++) w[e] = to_bf16(acc[cb][4 * g4 + e] * inv);
+      *(bf16x4*)(obuf + tile_off<D>(l32, cb * 32 + 8 * g4 + 4 * h32)) = w;
+    }
+  __syncthreads();
+  constexpr int CPR_O = D / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < 32 * CPR_O / 64; i++) {
+    const int p = i * 64 + lane;
+    const int r = p / CPR_O, ch = p % CPR_O;
+    const int row = qw0 + r;
+    const i32x4 val = *(const i32x4*)(obuf + r * (D * 2) + ((ch ^ swz<D>(r)) << 4));
+    if ((!LEAD_PAD || row >= 0) && row < Nq) {
+      i32x4* dst = (i32x4*)(a.o + q_head + (size_t)row * D + ch * 8);
+#if ATTN_FWD_O_STAGE == 2
+      __builtin_nontemporal_store(val, dst);
+#else
+      *dst = val;
+#endif
+    }
+  }
+  if ((!LEAD_PAD || qi >= 0) && qi < Nq && a.lse != nullptr && h32 == 0)
+    a.lse[lse_row + qi] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+#else
   if ((!LEAD_PAD || qi >= 0) && qi < Nq) {
     __bf16* orow = a.o + q_head + (size_t)qi * D;
 #pragma unroll
@@ -929,6 +972,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       }
     if (a.lse != nullptr && h32 == 0) a.lse[lse_row + qi] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
   }
+#endif
 }
 
 template <int D, bool CAUSAL, bool VARLEN = false, bool PAGED = false>
