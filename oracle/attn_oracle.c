@@ -16,7 +16,7 @@
  *   O[b,h,i,:] = sum_j softmax_j(s[i][:]) * V[b,kv(h),j,:]
  *   LSE[b,h,i] = log sum_j exp(s[i][j])                      (natural log)
  *
- * Readings taken where the pages are silent (each listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - causal visibility is bottom-right aligned: j <= i + (Nk - Nq);
  *   - grouped-query heads: kv(h) = h / (Hq / Hkv);
  *   - a row with no visible key has O = 0 and LSE = -inf (gradients 0);

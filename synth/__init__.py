@@ -5,7 +5,7 @@ tensors from a seeded numpy generator, rounds them to bfloat16 when asked, and
 picks sampled row indices.  Both sides of every comparison receive the same
 bits from here.
 
-Recipe (also stated in the design doc):
+Recipe:
   * ``numpy.random.default_rng(seed).standard_normal(shape, float32)``, drawn
     in the order the caller lists the tensors (Q, K, V, dO by convention);
   * bf16 inputs are those fp32 draws rounded to nearest-even bfloat16; the

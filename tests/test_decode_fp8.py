@@ -1,8 +1,8 @@
 """Split-KV decode over an FP8 (OCP E4M3) KV cache with a scale per kv head.
 
 FP8 KV caches are what the fastest engine the page "Tang Project Derives GPU
-Kernels via IR ..." compares against serves (section "Details"); the surveyed
-next row is decode reading such a cache, half the bytes of bf16.
+Kernels via IR ..." compares against serves (section "Details"); decoding
+from such a cache reads half the bytes of bf16.
 
 CPU: the oracle's E4M3 decoder against values the format definition fixes,
 the test-input encoder against that decoder (round trip, ties to even,
