@@ -155,7 +155,7 @@ attn_status attn_fwd_varlen_paged(const void* q, const void* k_cache, const void
  * attn_decode_num_splits returns the automatic plan: the power of two (1 to
  * 64) that minimises a cost model of the decode (per-workgroup streaming rate,
  * whole-device HBM rate, cost of each extra chunk and of the merge launch),
- * so a chunk per (stream, kv head) from about 128 (stream, kv head) pairs up.
+ * so a chunk per (stream, kv head) from about 160 (stream, kv head) pairs up.
  * attn_decode_workspace_bytes(..., num_splits) is enough for this entry point,
  * for attn_decode_splitkv_fp8 (whose plan models the FP8 kernel) and for
  * attn_decode_paged (Nk = its max_seq_len) at the same num_splits.

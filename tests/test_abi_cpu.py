@@ -323,11 +323,13 @@ def test_split_plan_and_workspace():
         # enough for this plan (and the FP8 entry point's, which may split more)
         assert ws >= (0 if s == 1 else B * 32 * s * (128 + 2) * 4)
         assert am.decode_workspace_bytes(B, 32, 8, L, 128, 1) == 0
-    # the cost model: from 16 streams x 8 kv heads up the cache is streamed by
-    # enough workgroups without splitting; one stream splits into 8..32 chunks
-    # of its 4096 keys; plans are powers of two; the single-launch path, with
-    # no merge launch to pay for, splits at least as much
-    assert n(48, 32, 8, 4096, 128) == 1 and n(16, 32, 8, 4096, 128) == 1 and n(48, 32, 8, 512, 128) == 1
+    # the cost model: from 20 streams x 8 kv heads up the cache is streamed by
+    # enough workgroups without splitting, 16 streams of 4096 keys take two
+    # chunks; one stream splits into 8..32 chunks of its 4096 keys; plans are
+    # powers of two; the single-launch path, with no merge launch to pay for,
+    # splits at least as much
+    assert n(48, 32, 8, 4096, 128) == 1 and n(20, 32, 8, 4096, 128) == 1 and n(48, 32, 8, 512, 128) == 1
+    assert n(16, 32, 8, 4096, 128) == 2
     assert 8 <= n(1, 32, 8, 4096, 128) <= 32
     for B in (1, 2, 4, 8, 16, 48):
         for L in (1, 100, 512, 1024, 2048, 4096, 32768):
