@@ -44,8 +44,9 @@ struct SplitPlan {
 // decode, with constants measured on MI355X at d = 128 (a sweep of every
 // split count at 1..48 streams x 1024..16384 keys, K/V streamed with the
 // non-temporal load policy):
-//   - one workgroup streams its chunk at ~85 keys/us (bf16 cache; ~92 for
-//     the FP8 kernel, which widens the codes in registers) after ~2 us of
+//   - one workgroup streams its chunk at ~85 keys/us (bf16 or FP8 cache:
+//     the FP8 kernel reads half the bytes but widens the codes in registers)
+//     after ~2 us of
 //     start-up, and the workgroups of a launch run in waves of one per CU
 //     (two for the FP8 kernel, whose tiles take half the LDS);
 //   - the whole decode reads at most ~6.5 TB/s;
@@ -67,7 +68,7 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int request
   } else {
     constexpr double kHbmBytesPerUs = 6.5e6, kWgStartUs = 2.0, kFoldUsPerSplit = 0.5, kMergeLaunchUs = 4.0;
     constexpr double kCallFloorUs = 15.0;
-    const double keys_per_us = fp8 ? 92.0 : 85.0;
+    constexpr double keys_per_us = 85.0;
     const double slots = kNumCUs * (fp8 ? 2.0 : 1.0);
     const double units = (double)(B * Hkv);
     const double key_bytes = 2.0 * (double)d * (fp8 ? 1.0 : 2.0);  // K and V
