@@ -41,24 +41,26 @@ struct SplitPlan {
 };
 
 // Choose the number of key chunks per (b, kv head) from a cost model of the
-// decode, with constants measured on MI355X at d = 128 (a sweep of every
-// split count at 1..48 streams x 1024..16384 keys, K/V streamed with the
-// non-temporal load policy):
-//   - one workgroup streams its chunk at ~85 keys/us (bf16 or FP8 cache:
-//     the FP8 kernel reads half the bytes but widens the codes in registers)
-//     after ~2 us of
-//     start-up, and the workgroups of a launch run in waves of one per CU
-//     (two for the FP8 kernel, whose tiles take half the LDS);
+// decode, with constants fitted on MI355X at d = 128 to the measured time of
+// every split count (1..64) at 1..48 streams x 512..16384 keys, both entry
+// points, K/V streamed with the non-temporal load policy (the fit minimises
+// the summed time of the picks; the points it changed were then re-measured
+// against the earlier plan in a second job):
+//   - a bf16 workgroup streams its chunk at ~80 keys/us after ~3 us of
+//     start-up, and the workgroups of a launch run in waves of one per CU;
+//     the FP8 kernel (two workgroups per CU, half the bytes per key, the
+//     codes widened in registers) keeps its own calibration, ~85 keys/us
+//     after ~2 us;
 //   - the whole decode reads at most ~6.5 TB/s;
 //   - each extra chunk costs ~0.5 us in the fold, and the two-launch path a
-//     further ~4 us for the merge launch;
-//   - a decode call takes ~15 us whatever it streams (launch and
-//     synchronisation), so a cache the unsplit plan streams in less is not
-//     split (one stream of 1024 keys: 15.8 us unsplit, 19.1 us in 4 chunks).
+//     further ~6 us (FP8: ~4 us) for the merge launch;
+//   - a cache the unsplit plan streams in less than ~10 us (FP8: ~15 us) is
+//     not split: the call's launch and synchronisation dominate it (FP8, one
+//     stream of 1024 keys: 12.9 us unsplit, 16.1 us in four chunks).
 // Candidates are 1, 2, 4, ... chunks of at least one key tile, at most 64;
 // a larger count must beat the smaller by 5 % (the model's resolution).
 // Splitting pays only where too few workgroups would stream the cache: from
-// 16 streams x 8 kv heads up a bf16 cache takes one chunk per (b, kv head).
+// 20 streams x 8 kv heads up a bf16 cache takes one chunk per (b, kv head).
 SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int requested, bool fused, bool fp8) {
   const int tile = attn::kDecodeTile;
   const int64_t tiles = Nk > 0 ? (Nk + tile - 1) / tile : 1;
@@ -66,9 +68,11 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int request
   if (requested > 0) {
     s = requested;
   } else {
-    constexpr double kHbmBytesPerUs = 6.5e6, kWgStartUs = 2.0, kFoldUsPerSplit = 0.5, kMergeLaunchUs = 4.0;
-    constexpr double kCallFloorUs = 15.0;
-    constexpr double keys_per_us = 85.0;
+    constexpr double kHbmBytesPerUs = 6.5e6, kFoldUsPerSplit = 0.5;
+    const double keys_per_us = fp8 ? 85.0 : 80.0;
+    const double wg_start_us = fp8 ? 2.0 : 3.0;
+    const double merge_launch_us = fp8 ? 4.0 : 6.0;
+    const double call_floor_us = fp8 ? 15.0 : 10.0;
     const double slots = kNumCUs * (fp8 ? 2.0 : 1.0);
     const double units = (double)(B * Hkv);
     const double key_bytes = 2.0 * (double)d * (fp8 ? 1.0 : 2.0);  // K and V
@@ -78,13 +82,13 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int request
     for (int64_t c = 1; c <= std::min<int64_t>(tiles, 64); c *= 2) {
       const double chunk_keys = (double)(((tiles + c - 1) / c) * tile);
       const double waves = std::ceil(units * (double)c / slots);
-      double t = std::max(waves * (kWgStartUs + chunk_keys / keys_per_us), hbm_us);
-      if (c > 1) t += kFoldUsPerSplit * (double)c + (fused ? 0.0 : kMergeLaunchUs);
+      double t = std::max(waves * (wg_start_us + chunk_keys / keys_per_us), hbm_us);
+      if (c > 1) t += kFoldUsPerSplit * (double)c + (fused ? 0.0 : merge_launch_us);
       if (c == 1 || t < 0.95 * best) {
         best = t;
         s = (int)c;
       }
-      if (c == 1 && t < kCallFloorUs) break;
+      if (c == 1 && t < call_floor_us) break;
     }
   }
   if (s > tiles) s = (int)tiles;
