@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_varlen_paged.restype = ci
     L.attn_decode_paged.argtypes = [vp] * 7 + [i64] * 8 + [f32, ci, vp, sz, vp]
     L.attn_decode_paged.restype = ci
+    L.attn_decode_paged_fused.argtypes = L.attn_decode_paged.argtypes
+    L.attn_decode_paged_fused.restype = ci
+    L.attn_decode_paged_fused_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
+    L.attn_decode_paged_fused_workspace_bytes.restype = sz
     L.attn_decode_splitkv_fp8.argtypes = [vp] * 7 + [i64] * 6 + [f32, ci, vp, sz, vp]
     L.attn_decode_splitkv_fp8.restype = ci
     L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
@@ -369,12 +373,7 @@ def attn_fwd_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_le
     return o, (lse if want_lse else None)
 
 
-def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale=None, num_splits: int = 0,
-                      workspace=None, out=None, lse=None, want_lse: bool = True):
-    """Split-KV decode over a paged bf16 KV cache.  q [B, Hq, 1, d]; k_cache,
-    v_cache [num_pages, Hkv, page_size, d]; block_table int32 [B, max_pages];
-    seq_lens int32 [B]; max_seq_len >= every seq_lens entry.  Returns
-    (o [B, Hq, 1, d], lse [B, Hq, 1])."""
+def _paged_args(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace, want_lse):
     _check_dev(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("q must be [B, Hq, 1, d] and k_cache, v_cache [num_pages, Hkv, page_size, d]")
@@ -394,6 +393,17 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: i
     o = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    return B, Hq, Hkv, d, num_pages, page, o, lse
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale=None, num_splits: int = 0,
+                      workspace=None, out=None, lse=None, want_lse: bool = True):
+    """Split-KV decode over a paged bf16 KV cache.  q [B, Hq, 1, d]; k_cache,
+    v_cache [num_pages, Hkv, page_size, d]; block_table int32 [B, max_pages];
+    seq_lens int32 [B]; max_seq_len >= every seq_lens entry.  Returns
+    (o [B, Hq, 1, d], lse [B, Hq, 1])."""
+    B, Hq, Hkv, d, num_pages, page, o, lse = _paged_args(q, k_cache, v_cache, block_table, seq_lens, out, lse,
+                                                        workspace, want_lse)
     if workspace is None:
         need = decode_workspace_bytes(B, Hq, Hkv, int(max_seq_len), d, num_splits)
         if need > 0:
@@ -405,6 +415,32 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: i
                                  _ptr(workspace), ws_bytes, _stream())
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_paged")
+    return o, (lse if want_lse else None)
+
+
+def decode_paged_fused_workspace_bytes(B: int, Hq: int, Hkv: int, max_seq_len: int, d: int, num_splits: int = 0) -> int:
+    return int(lib().attn_decode_paged_fused_workspace_bytes(B, Hq, Hkv, max_seq_len, d, num_splits))
+
+
+def attn_decode_paged_fused(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale=None,
+                            num_splits: int = 0, workspace=None, out=None, lse=None, want_lse: bool = True):
+    """attn_decode_paged in one launch (the last chunk of each stream and kv
+    head to finish merges).  A workspace passed in must have been zeroed
+    before its first use (every call leaves its arrival counts zero); without
+    one a zeroed one is allocated.  Returns (o, lse)."""
+    B, Hq, Hkv, d, num_pages, page, o, lse = _paged_args(q, k_cache, v_cache, block_table, seq_lens, out, lse,
+                                                        workspace, want_lse)
+    if workspace is None:
+        need = decode_paged_fused_workspace_bytes(B, Hq, Hkv, int(max_seq_len), d, num_splits)
+        if need > 0:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_paged_fused(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                       _ptr(o), _ptr(lse) if want_lse else None, B, Hq, Hkv, d, num_pages, page,
+                                       block_table.shape[1], int(max_seq_len), _scale(scale, d), int(num_splits),
+                                       _ptr(workspace), ws_bytes, _stream())
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_paged_fused")
     return o, (lse if want_lse else None)
 
 

@@ -107,16 +107,16 @@ SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t Nk, int64_t d, int request
 // and with fewer (stream, kv head) pairs than CUs, enough chunks of at least
 // 1024 keys to give each CU one (16 streams of 512..4096: 42.7 us in two
 // chunks against 51.9 in one).
-SplitPlan paged_plan(int64_t B, int64_t Hkv, int64_t max_seq_len, int64_t d, int requested) {
+SplitPlan paged_plan(int64_t B, int64_t Hkv, int64_t max_seq_len, int64_t d, int requested, bool fused = false) {
   if (requested == 0) {
-    int64_t s = plan_splits(B, Hkv, max_seq_len, d, 0, false, false).splits;
+    int64_t s = plan_splits(B, Hkv, max_seq_len, d, 0, fused, false).splits;
     s = std::max<int64_t>(s, max_seq_len / 4096);
     const int64_t pairs = B * Hkv;
     if (pairs > 0 && pairs < kNumCUs)
       s = std::max<int64_t>(s, std::min<int64_t>((kNumCUs + pairs - 1) / pairs, max_seq_len / 1024));
     requested = (int)std::min<int64_t>(s, 64);
   }
-  return plan_splits(B, Hkv, max_seq_len, d, requested, false, false);
+  return plan_splits(B, Hkv, max_seq_len, d, requested, fused, false);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -252,6 +252,14 @@ size_t attn_decode_fused_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int
   return kDecodeCountBytes + parts;
 }
 
+size_t attn_decode_paged_fused_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seq_len, int64_t d,
+                                               int num_splits) {
+  if (!dims_ok(B, Hq, Hkv, 1, max_seq_len) || (d != 64 && d != 128) || num_splits < 0) return 0;
+  const size_t parts = partial_bytes(B, Hq, Hkv, d, paged_plan(B, Hkv, max_seq_len, d, num_splits, true));
+  if (parts == 0) return 0;
+  return kDecodeCountBytes + parts;
+}
+
 }  // extern "C"
 
 namespace {
@@ -349,11 +357,14 @@ attn_status attn_decode_splitkv_fused(const void* q, const void* k, const void* 
                        workspace, workspace_bytes, dtype, stream);
 }
 
-attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
-                              const int32_t* seq_lens, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
-                              int64_t d, int64_t num_pages, int64_t page_size, int64_t max_pages,
-                              int64_t max_seq_len, float scale, int num_splits, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+attn_status paged_common(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         const int32_t* seq_lens, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                         int64_t num_pages, int64_t page_size, int64_t max_pages, int64_t max_seq_len, float scale,
+                         int num_splits, void* workspace, size_t workspace_bytes, void* stream, bool fused) {
   if (num_pages < 0 || page_size < 0 || max_pages < 0 || max_seq_len < 0) return ATTN_ERR_INVALID;
   attn_status st = check_common(B, Hq, Hkv, 1, max_seq_len, d, scale, ATTN_BF16);
   if (st != ATTN_OK) return st;
@@ -366,7 +377,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   // keys can be read only if there are pages to read them from
   if (max_seq_len > 0 && (max_pages == 0 || num_pages == 0 || !k_cache || !v_cache || !block_table))
     return ATTN_ERR_INVALID;
-  SplitPlan sp = paged_plan(B, Hkv, max_seq_len, d, num_splits);
+  SplitPlan sp = paged_plan(B, Hkv, max_seq_len, d, num_splits, fused);
   attn::DecodeProblem p{};
   p.q = q;
   p.k = k_cache;
@@ -382,11 +393,19 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   p.num_splits = sp.splits;
   p.chunk = sp.chunk;
   if (sp.splits > 1) {
-    const size_t need = partial_bytes(B, Hq, Hkv, d, sp);
+    const size_t need = (fused ? kDecodeCountBytes : 0) + partial_bytes(B, Hq, Hkv, d, sp);
     if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    // the arrival counts take device atomics: 4-byte alignment
+    if (fused && ((uintptr_t)workspace & 3) != 0) return ATTN_ERR_INVALID;
+    char* ws = (char*)workspace;
+    if (fused) {
+      if (B * Hkv > kDecodeMaxPairs) return ATTN_ERR_UNSUPPORTED;
+      p.counters = (unsigned*)ws;
+      ws += kDecodeCountBytes;
+    }
     const size_t rows = (size_t)B * Hq * sp.splits;
-    p.part_acc = (float*)workspace;
-    p.part_ml = (float*)((char*)workspace + align256(rows * d * sizeof(float)));
+    p.part_acc = (float*)ws;
+    p.part_ml = (float*)(ws + align256(rows * d * sizeof(float)));
   }
   if (max_seq_len > 0) {
     p.block_table = block_table;
@@ -399,6 +418,28 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
     p.k = p.v = nullptr;
   }
   return attn::launch_decode(p, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                              int64_t d, int64_t num_pages, int64_t page_size, int64_t max_pages,
+                              int64_t max_seq_len, float scale, int num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return paged_common(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv, d, num_pages, page_size,
+                      max_pages, max_seq_len, scale, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+attn_status attn_decode_paged_fused(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                    int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t num_pages,
+                                    int64_t page_size, int64_t max_pages, int64_t max_seq_len, float scale,
+                                    int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return paged_common(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv, d, num_pages, page_size,
+                      max_pages, max_seq_len, scale, num_splits, workspace, workspace_bytes, stream, true);
 }
 
 attn_status attn_decode_splitkv_fp8(const void* q, const void* k, const void* v, const float* k_scale,

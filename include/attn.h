@@ -266,6 +266,33 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
                               size_t workspace_bytes, void* stream);
 
 /*
+ * The paged decode in one launch: attn_decode_paged's arguments, rules and
+ * result for the same num_splits (the same kernel and fold, so the same
+ * bits), with the chunks merged as attn_decode_splitkv_fused merges them:
+ * the last chunk of each (stream, kv head) to finish folds the others' states
+ * in index order and writes o and lse, so no merge kernel is launched.
+ *   Workspace attn_decode_paged_fused_workspace_bytes bytes (0 when the plan
+ *             has one chunk), 4-byte aligned (ATTN_ERR_INVALID otherwise);
+ *             its first 64 KiB hold the arrival counts, one per (stream, kv
+ *             head), so B * Hkv <= 16384 when the plan has more than one
+ *             chunk (ATTN_ERR_UNSUPPORTED otherwise), and the partial states
+ *             follow.  The counts must be zero before the first call on that
+ *             memory; every call that completes leaves them zero.  Calls
+ *             that share a workspace must not run concurrently (stream order
+ *             suffices), and memory used by another entry point must be
+ *             zeroed again before it serves this one.
+ *   Plan     attn_decode_paged's rules on the single-launch model, which
+ *             has no merge launch to pay for and so may split more.
+ */
+size_t attn_decode_paged_fused_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seq_len, int64_t d,
+                                               int num_splits);
+attn_status attn_decode_paged_fused(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                    int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t num_pages,
+                                    int64_t page_size, int64_t max_pages, int64_t max_seq_len, float scale,
+                                    int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Split-KV decode over an FP8 KV cache: k and v hold OCP FP8 E4M3 codes
  * (1 byte per element, [B,Hkv,Nk,d]; 0x7F / 0xFF are NaN and propagate), and
  * kv head h's values are k_scale[h] * code and v_scale[h] * code (k_scale,

@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_varlen", "attn_decode_splitkv", "attn_decode_splitkv_fp8", "attn_bwd",
               "attn_decode_splitkv_fused", "attn_decode_fused_workspace_bytes", "attn_decode_workspace_bytes",
-              "attn_decode_paged", "attn_fwd_varlen_paged",
+              "attn_decode_paged", "attn_fwd_varlen_paged", "attn_decode_paged_fused",
+              "attn_decode_paged_fused_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_decode_num_splits", "attn_strerror"):
         assert n in names
 
@@ -243,9 +244,9 @@ def test_fwd_varlen_paged_empty_launches_nothing():
 
 
 def decp(q=P, k=P, v=P, bt=P, sl=P, o=P, lse=P, B=4, Hq=32, Hkv=8, d=128, pages=100, page=64, maxp=20,
-         maxl=1280, scale=0.088, splits=0, ws=P, ws_bytes=1 << 30):
-    return am.lib().attn_decode_paged(q, k, v, bt, sl, o, lse, B, Hq, Hkv, d, pages, page, maxp, maxl, scale, splits,
-                                      ws, ws_bytes, None)
+         maxl=1280, scale=0.088, splits=0, ws=P, ws_bytes=1 << 30, fn="attn_decode_paged"):
+    return getattr(am.lib(), fn)(q, k, v, bt, sl, o, lse, B, Hq, Hkv, d, pages, page, maxp, maxl, scale, splits,
+                                 ws, ws_bytes, None)
 
 
 @no_gpu
@@ -272,6 +273,21 @@ def decp(q=P, k=P, v=P, bt=P, sl=P, o=P, lse=P, B=4, Hq=32, Hkv=8, d=128, pages=
 )
 def test_decode_paged_rejects(kw, code):
     assert decp(**kw) == code
+    assert decp(fn="attn_decode_paged_fused", **kw) == code
+
+
+@no_gpu
+def test_decode_paged_fused_workspace_rules():
+    B, Hq, Hkv, L, d = 4, 32, 8, 1280, 128
+    need = am.decode_paged_fused_workspace_bytes(B, Hq, Hkv, L, d, 4)
+    # the arrival counts (64 KiB) come first, then four chunks' partial states
+    assert need == 65536 + am.decode_workspace_bytes(B, Hq, Hkv, L, d, 4)
+    f = dict(fn="attn_decode_paged_fused", splits=4)
+    assert decp(ws_bytes=need - 1, **f) == am.ATTN_ERR_WORKSPACE
+    assert decp(ws=ctypes.c_void_p(0x1002), ws_bytes=need, **f) == am.ATTN_ERR_INVALID   # not 4-byte aligned
+    assert decp(B=2049, Hkv=8, Hq=8, maxl=L, ws_bytes=1 << 40, **f) == am.ATTN_ERR_UNSUPPORTED  # > 16384 counts
+    assert am.decode_paged_fused_workspace_bytes(B, Hq, Hkv, L, d, 1) == 0
+    assert am.decode_paged_fused_workspace_bytes(48, Hq, Hkv, 4096, d, 0) == 0   # one chunk at 48 streams
 
 
 @no_gpu

@@ -145,3 +145,69 @@ def test_paged_in_order_equals_dense_decode(splits):
     torch.cuda.synchronize()
     assert torch.equal(o_p, o_d)
     assert torch.equal(l_p, l_d)
+
+
+# ---------------------------------------------------------------- single launch
+
+def _run_fused(q, kc, vc, table, lens, used, splits, workspace=None):
+    import torch
+
+    import attention_online_softmax_attn_amd as am
+    from gpu_helpers import dev
+
+    kd, vd = dev(kc, True), dev(vc, True)
+    mask = torch.from_numpy(~used).cuda()[:, None, :, None].expand(kd.shape)
+    kd = kd.masked_fill(mask, float("nan")).contiguous()
+    vd = vd.masked_fill(mask, float("nan")).contiguous()
+    return am.attn_decode_paged_fused(dev(q, True), kd, vd, torch.from_numpy(table).cuda(),
+                                      torch.from_numpy(lens).cuda(), int(lens.max()) if len(lens) else 0,
+                                      num_splits=splits, workspace=workspace)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("splits", [1, 3])
+def test_paged_fused_equals_two_launch_bits(case, splits):
+    import torch
+
+    lens, Hq, Hkv, page, d = CASES[case]
+    print(f"paged decode, one launch vs two: lens[:8]={lens[:8]} Hq={Hq} Hkv={Hkv} page={page} d={d} splits={splits}",
+          flush=True)
+    q, kc, vc, table, lens_a, used = synth.paged_kv_inputs(900 + case, lens, Hq, Hkv, page, d)
+    o1, l1 = _run(q, kc, vc, table, lens_a, used, splits)
+    o2, l2 = _run_fused(q, kc, vc, table, lens_a, used, splits)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+
+
+@pytest.mark.gpu
+def test_paged_fused_auto_plan_and_workspace_reuse(oracle_mod):
+    import torch
+
+    import attention_online_softmax_attn_amd as am
+    from gpu_helpers import TOL_LSE_BF16, TOL_O_BF16, assert_close, host
+
+    # 16 streams of unequal length: the plan splits (fewer (stream, kv head)
+    # pairs than CUs), so the last chunk of each pair merges
+    rng = np.random.default_rng(16)
+    lens = [int(x) for x in rng.integers(512, 4097, size=16)]
+    assert am.decode_paged_fused_workspace_bytes(16, 32, 8, max(lens), 128) > 65536
+    q, kc, vc, table, lens_a, used = synth.paged_kv_inputs(960, lens, 32, 8, 64, 128)
+    ws = torch.zeros(am.decode_paged_fused_workspace_bytes(16, 32, 8, max(lens), 128), dtype=torch.uint8,
+                     device="cuda")
+    print(f"paged decode in one launch, 16 streams, {sum(lens)} keys, workspace {ws.numel()} bytes", flush=True)
+    o, lse = _run_fused(q, kc, vc, table, lens_a, used, 0, workspace=ws)
+    torch.cuda.synchronize()
+    eo, el = oracle.decode_paged(q, kc, vc, table, lens_a, 1.0 / math.sqrt(128))
+    assert_close("O", host(o), eo, TOL_O_BF16)
+    assert_close("LSE", host(lse), el, TOL_LSE_BF16)
+    assert int(ws[:65536].count_nonzero()) == 0      # every arrival count back at zero
+    # the same workspace serves a smaller call
+    q2, kc2, vc2, table2, lens2, used2 = synth.paged_kv_inputs(961, lens[:5], 32, 8, 64, 128)
+    o2, l2 = _run_fused(q2, kc2, vc2, table2, lens2, used2, 0, workspace=ws)
+    torch.cuda.synchronize()
+    e2, f2 = oracle.decode_paged(q2, kc2, vc2, table2, lens2, 1.0 / math.sqrt(128))
+    assert_close("O", host(o2), e2, TOL_O_BF16)
+    assert_close("LSE", host(l2), f2, TOL_LSE_BF16)
+    assert int(ws[:65536].count_nonzero()) == 0
