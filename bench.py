@@ -22,7 +22,8 @@ packed batch of 16 sequences (attn_fwd_varlen); decode_fp8 = the decode shape
 over an FP8 E4M3 KV cache (attn_decode_splitkv_fp8); decode_fused = the decode
 shape in one launch (attn_decode_splitkv_fused, the last split merges);
 decode_paged = 48 streams of 512..4096 keys each (seeded) in a paged cache of
-64-key pages through a block table (attn_decode_paged); varlen_paged = the
+64-key pages through a block table (attn_decode_paged); decode_paged_fused =
+the same paged batch in one launch (attn_decode_paged_fused); varlen_paged = the
 varlen batch with each sequence's keys in 64-key pages of a shuffled cache
 (attn_fwd_varlen_paged).
 
@@ -34,7 +35,8 @@ one JSON line per point with median / p10 / p90 / min over >= 50 calls, inputs
 rotating over copies of >= 512 MiB so that no call finds them in the MALL.
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu]
-                       [--paths fwd,decode,bwd[,varlen][,decode_fp8][,decode_fused][,decode_paged][,varlen_paged]]
+                       [--paths fwd,decode,bwd[,varlen][,decode_fp8][,decode_fused][,decode_paged]
+                                [,decode_paged_fused][,varlen_paged]]
        python bench.py --sweep
 """
 from __future__ import annotations
@@ -59,6 +61,10 @@ BACKWARD = dict(B=4, H=16, N=2048, d=128, causal=True, seed=5)
 # opt-in path (--paths ...,varlen): chunked prefill of 16 sequences, each
 # appending 512..2048 new tokens to a cached history of 0..4096 tokens
 VARLEN = dict(n=16, lq=(512, 2048), hist=(0, 4096), Hq=32, Hkv=8, d=128, seed=6, len_seed=7)
+# every path --paths may name, in the order a step runs them
+PATH_NAMES = ("fwd", "decode", "bwd", "decode_fp8", "decode_fused", "decode_paged", "decode_paged_fused", "varlen",
+              "varlen_paged")
+
 # opt-in path (--paths ...,decode_paged): 48 streams of unequal length in 64-key pages
 PAGED = dict(B=48, Hq=32, Hkv=8, lens=(512, 4096), page=64, d=128, seed=9, len_seed=10)
 
@@ -172,7 +178,7 @@ def setup(paths):
         q, k8, v8, ks, vs = synth.fp8_kv_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["L"], c["d"])
         st["decode_fp8"] = (to_dev(q), torch.from_numpy(k8).cuda(), torch.from_numpy(v8).cuda(),
                             torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda())
-    if "decode_paged" in paths:
+    if "decode_paged" in paths or "decode_paged_fused" in paths:
         import numpy as np
         import torch
 
@@ -323,6 +329,14 @@ def run_gpu(paths, steps, warmup):
         ws = am.decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], st["decode_paged"][5], c["d"], 0)
         dev_out["decode_paged"] = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"),
                                    torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda"))
+    if "decode_paged_fused" in paths:
+        q = st["decode_paged"][0]
+        c = PAGED
+        ws = am.decode_paged_fused_workspace_bytes(c["B"], c["Hq"], c["Hkv"], st["decode_paged"][5], c["d"], 0)
+        # the arrival counts start at zero; every call leaves them zero
+        dev_out["decode_paged_fused"] = (torch.empty_like(q),
+                                         torch.empty(q.shape[:3], dtype=torch.float32, device="cuda"),
+                                         torch.zeros(max(ws, 1), dtype=torch.uint8, device="cuda"))
     if "varlen" in paths:
         q = st["varlen"][0]
         dev_out["varlen"] = (torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda"))
@@ -352,6 +366,10 @@ def run_gpu(paths, steps, warmup):
             q, kc, vc, bt, sl, ml = st["decode_paged"]
             o, lse, ws = dev_out["decode_paged"]
             am.attn_decode_paged(q, kc, vc, bt, sl, ml, workspace=ws, out=o, lse=lse)
+        elif name == "decode_paged_fused":
+            q, kc, vc, bt, sl, ml = st["decode_paged"]
+            o, lse, ws = dev_out["decode_paged_fused"]
+            am.attn_decode_paged_fused(q, kc, vc, bt, sl, ml, workspace=ws, out=o, lse=lse)
         elif name == "varlen":
             q, k, v, cq, ck, mq = st["varlen"]
             o, lse = dev_out["varlen"]
@@ -365,8 +383,7 @@ def run_gpu(paths, steps, warmup):
             o, lse, dq, dk, dv, ws = dev_out["bwd"]
             am.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
 
-    order = [p for p in ("fwd", "decode", "bwd", "decode_fp8", "decode_fused", "decode_paged", "varlen", "varlen_paged")
-             if p in paths]
+    order = [p for p in PATH_NAMES if p in paths]
     for _ in range(warmup):
         for p in order:
             run_path(p)
@@ -677,6 +694,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     paths = [p for p in args.paths.split(",") if p]
+    unknown = [p for p in paths if p not in PATH_NAMES]
+    if unknown:
+        print(f"bench.py: unknown path(s) {', '.join(unknown)}; known: {', '.join(PATH_NAMES)}", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -734,15 +755,17 @@ def main():
                                      "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
                                      "shape": "48 streams, Hq=32 Hkv=8 d=128, 4096 keys, one launch"}
         total_flops += decode_flops(c["B"], c["Hq"], c["L"], c["d"])
-    if "decode_paged" in paths:
+    for name, how in (("decode_paged", ""), ("decode_paged_fused", ", one launch")):
+        if name not in paths:
+            continue
         c = PAGED
         lens = st["decode_paged_lens"]
         b = sum(2.0 * c["Hkv"] * n * c["d"] * 2 for n in lens) + 2.0 * c["B"] * c["Hq"] * c["d"] * 2 + c["B"] * c["Hq"] * 4
-        t = sum(per["decode_paged"]) / len(per["decode_paged"])
-        out_paths["decode_paged"] = {"ms": round(t, 4), "ms_median": round(med(per["decode_paged"]), 4),
-                                     "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
-                                     "shape": f"48 streams of 512..4096 keys ({sum(lens)} in all), 64-key pages, "
-                                              "Hq=32 Hkv=8 d=128"}
+        t = sum(per[name]) / len(per[name])
+        out_paths[name] = {"ms": round(t, 4), "ms_median": round(med(per[name]), 4),
+                           "gbs": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / PEAK_HBM_GBS, 4),
+                           "shape": f"48 streams of 512..4096 keys ({sum(lens)} in all), 64-key pages, "
+                                    f"Hq=32 Hkv=8 d=128{how}"}
         total_flops += sum(decode_flops(1, c["Hq"], n, c["d"]) for n in lens)
     if "varlen" in paths:
         c = VARLEN

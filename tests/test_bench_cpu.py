@@ -22,6 +22,13 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in r.stderr
 
 
+def test_an_unknown_path_name_is_refused_with_the_known_ones():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--paths", "fwd,decode_pagd"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "decode_pagd" in r.stderr and "decode_paged_fused" in r.stderr
+
+
 def test_work_formulas_at_the_configured_shapes():
     # causal prefill at 44032 tokens, 32 query heads, d = 128: 15.88 TFLOP
     assert bench.fwd_flops(1, 32, 44032, 44032, 128, True) == pytest.approx(15.88e12, rel=1e-3)
