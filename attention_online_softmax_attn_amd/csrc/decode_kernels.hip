@@ -89,22 +89,51 @@ __device__ __forceinline__ float load_agent(const float* p) {
 // single-launch path share it, so both give the same bits.  AGENT: the
 // states were written by this same launch on other XCDs (device-scope
 // loads); otherwise by an earlier kernel (plain loads, which may hit L2).
-// The loops are unrolled so that several loads are in flight at once.
+// Up to kFoldBatch splits are loaded all at once (one memory round trip
+// instead of one for the maxima and another for the sums); more splits take
+// the two unrolled loops.  Either way the fold is the same sequence of
+// operations, so the bits do not depend on the path.
+constexpr int kFoldBatch = 8;
 template <int D, bool AGENT>
 __device__ __forceinline__ void fold_split_states(const DecArgs& a, size_t row, int col) {
   auto ld = [](const float* p) { return AGENT ? load_agent(p) : *p; };
   const float* ml = a.part_ml + row * a.S * 2;
   const float* pa = a.part_acc + row * a.S * D + col;
   float M = kNegInf;
-#pragma unroll 8
-  for (int s = 0; s < a.S; s++) M = fmaxf(M, ld(ml + 2 * s));
   float L = 0.0f, A = 0.0f;
+  if (a.S <= kFoldBatch) {
+    float m[kFoldBatch], l[kFoldBatch], x[kFoldBatch];
+#pragma unroll
+    for (int s = 0; s < kFoldBatch; s++) {
+      m[s] = kNegInf;
+      l[s] = x[s] = 0.0f;
+      if (s < a.S) {
+        m[s] = ld(ml + 2 * s);
+        l[s] = ld(ml + 2 * s + 1);
+        x[s] = ld(pa + (size_t)s * D);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kFoldBatch; s++)
+      if (s < a.S) M = fmaxf(M, m[s]);
+#pragma unroll
+    for (int s = 0; s < kFoldBatch; s++) {
+      if (s < a.S) {
+        const float f = (m[s] == kNegInf) ? 0.0f : fast_exp2(m[s] - M);
+        L += f * l[s];
+        A += f * x[s];
+      }
+    }
+  } else {
 #pragma unroll 8
-  for (int s = 0; s < a.S; s++) {
-    const float ms = ld(ml + 2 * s);
-    const float f = (ms == kNegInf) ? 0.0f : fast_exp2(ms - M);
-    L += f * ld(ml + 2 * s + 1);
-    A += f * ld(pa + (size_t)s * D);
+    for (int s = 0; s < a.S; s++) M = fmaxf(M, ld(ml + 2 * s));
+#pragma unroll 8
+    for (int s = 0; s < a.S; s++) {
+      const float ms = ld(ml + 2 * s);
+      const float f = (ms == kNegInf) ? 0.0f : fast_exp2(ms - M);
+      L += f * ld(ml + 2 * s + 1);
+      A += f * ld(pa + (size_t)s * D);
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   a.o[row * D + col] = to_bf16(A * inv);
